@@ -14,6 +14,7 @@ are already decoded from storage; outputs are float64 and unrounded.
 from __future__ import annotations
 
 import math
+import struct
 
 
 def _sigmoid(u: float) -> float:
@@ -108,3 +109,42 @@ def rms_norm_row(c, g, eps: float):
         ss += v * v
     q = 1.0 / math.sqrt(ss / D + eps)
     return [(c[d] * q) * g[d] for d in range(D)]
+
+
+def f32(v: float) -> float:
+    """Round a Python float to the nearest fp32 value (ties to even)."""
+    return struct.unpack("<f", struct.pack("<f", v))[0]
+
+
+def bf16(v: float) -> float:
+    """Round to fp32, then to the nearest bf16 value (ties to even), as a Python float."""
+    u = struct.unpack("<I", struct.pack("<f", f32(v)))[0]
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return struct.unpack("<f", struct.pack("<I", u & 0xFFFFFFFF))[0]
+
+
+def combine_token_f32(h, x, post, comb, w, n: int, D: int, to_storage):
+    """Fused-kernel intermediates of one token under the fp32 reading.
+
+    Each post row is a = post_j * h (fp32), then a = fma(comb[i][j], x_i, a)
+    for i in stream order, stored with ``to_storage``; the combined row is
+    c = fma(w_j, o_j, c) from 0 in stream order, stored with ``to_storage``.
+    A fused multiply-add of fp32 operands is the fp32 rounding of the exact
+    product plus the addend (the product is exact in a Python float).
+    """
+    o = []
+    for j in range(n):
+        row = []
+        for d in range(D):
+            a = f32(post[j] * h[d])
+            for i in range(n):
+                a = f32(comb[i][j] * x[i][d] + a)
+            row.append(to_storage(a))
+        o.append(row)
+    c = []
+    for d in range(D):
+        acc = 0.0
+        for j in range(n):
+            acc = f32(w[j] * o[j][d] + acc)
+        c.append(to_storage(acc))
+    return o, c

@@ -301,6 +301,49 @@ def rms_norm(c, weight, eps: float) -> np.ndarray:
     return (c * q) * np.asarray(weight, dtype=np.float64)
 
 
+def fma32(a, b, c) -> np.ndarray:
+    """fp32 fused multiply-add round_f32(a * b + c), evaluated through float64.
+
+    The product of two fp32 values is exact in float64; the float64 sum is
+    exact unless the operands are about 2^21 apart in magnitude, where its
+    rounding is far below one fp32 unit, so the result is the correctly
+    rounded fp32 FMA except in (unobserved) double-rounding ties.
+    """
+    return (np.asarray(a, dtype=np.float32).astype(np.float64) * np.asarray(b, dtype=np.float32).astype(np.float64)
+            + np.asarray(c, dtype=np.float32).astype(np.float64)).astype(np.float32)
+
+
+def combine_intermediates(h, x, post, comb, w, dtype: str):
+    """The fused kernel's rounded intermediates (o [T, n, D], c [T, D]) as float64.
+
+    [P2] section 1: the post rows and the combined row are bf16 intermediates.
+    Reading: rounding a value to the storage type is a quantisation decision,
+    so it is taken from the same fp32 sums on both sides: each post row is
+    a = post_j * h, then a = fma(comb[i, j], x_i, a) for i = 0..n-1, rounded
+    to the storage type; the combined row is c = fma(w_j, o_j, c) for
+    j = 0..n-1 from c = 0, rounded to the storage type. (The all-float64 form
+    of the same formulas agrees to within the rounding of these
+    intermediates; a pin checks that bound.)
+    """
+    h32 = decode(h, dtype).astype(np.float32)
+    x32 = decode(x, dtype).astype(np.float32)
+    T, n, D = x32.shape
+    p32 = np.asarray(post, dtype=np.float32)
+    c32 = np.asarray(comb, dtype=np.float32)
+    w32 = np.asarray(w, dtype=np.float32)
+    o = np.empty((T, n, D), dtype=np.float64)
+    for j in range(n):
+        a = (p32[:, j:j + 1].astype(np.float64) * h32.astype(np.float64)).astype(np.float32)
+        for i in range(n):
+            a = fma32(c32[:, i, j:j + 1], x32[:, i, :], a)
+        o[:, j, :] = decode(encode(a, dtype), dtype)
+    acc = np.zeros((T, D), dtype=np.float32)
+    for j in range(n):
+        acc = fma32(w32[:, j:j + 1], o[:, j, :], acc)
+    c = decode(encode(acc, dtype), dtype)
+    return o, c
+
+
 def mhc_post_combine_norm(h, residual, post, comb, combine_w, norm_weight, *,
                           n: int, D: int, dtype: str, norm_eps: float, chunk: int = 1024):
     """Fused post mix + next-layer combine + RMSNorm -> (normalized [T, D], out [T, n, D]).
@@ -308,21 +351,27 @@ def mhc_post_combine_norm(h, residual, post, comb, combine_w, norm_weight, *,
     [P2] section 1: one row at a time, the post result is combined across the
     n streams into a bf16 ``collapsed`` row of D values, which is then
     RMS-normalised; [P2] section 2 stores it as ``normalized``.
-    Reading: out_j is the mhc_post result rounded to the residual dtype;
-    c[d] = sum_j w[j] * out_j[d] is rounded to the residual dtype (the bf16
-    intermediate); the RMSNorm runs on that rounded c and is rounded once.
-    combine_w [T, n] and norm_weight [D] are fp32.
+    Reading: out_j is the post result rounded to the residual dtype and c is
+    the combined row rounded to the residual dtype, both formed as
+    ``combine_intermediates`` states; the RMSNorm runs in float64 on that
+    rounded c and is rounded once. combine_w [T, n] and norm_weight [D] are
+    fp32.
     """
     T = np.asarray(residual).shape[0]
+    residual = _check_tokens(residual, T, (n, D), "residual")
+    h = _check_tokens(h, T, (D,), "h")
     w = _check_tokens(np.asarray(combine_w, dtype=np.float32), T, (n,), "combine_w")
     g = np.asarray(norm_weight, dtype=np.float32)
     if g.shape != (D,):
         raise ValueError(f"norm_weight has shape {g.shape}, expected {(D,)}")
-    out = mhc_post(h, residual, post, comb, n=n, D=D, dtype=dtype, chunk=chunk)
-    normalized = np.empty((T, D), dtype=out.dtype)
+    post = _check_tokens(np.asarray(post, dtype=np.float32), T, (n,), "post")
+    comb = _check_tokens(np.asarray(comb, dtype=np.float32), T, (n, n), "comb")
+    odt = np.uint16 if dtype == "bf16" else np.float32
+    out = np.empty((T, n, D), dtype=odt)
+    normalized = np.empty((T, D), dtype=odt)
     for t0 in range(0, T, chunk):
         sl = slice(t0, t0 + chunk)
-        o = decode(out[sl], dtype)
-        c = decode(encode(np.einsum("tj,tjd->td", w[sl].astype(np.float64), o), dtype), dtype)
+        o, c = combine_intermediates(h[sl], residual[sl], post[sl], comb[sl], w[sl], dtype)
+        out[sl] = encode(o, dtype)
         normalized[sl] = encode(rms_norm(c, g.astype(np.float64), norm_eps), dtype)
     return normalized, out

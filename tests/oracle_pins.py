@@ -342,23 +342,40 @@ def pin_combine_norm(O):
                                         np.array([[1, 0, 0, 0]], np.float32), gw, n=n, D=D, dtype="bf16",
                                         norm_eps=EPS)
         assert np.array_equal(nz[0], _bf16((cval / math.sqrt(cval * cval + EPS)) * gw.astype(np.float64)))
-    # brute force with explicit bf16 rounding of out and of the combined row
+    # brute force: scalar loops with the fp32 intermediates and bf16 storage rounding
     w = g.uniform(0, 1, (T, n)).astype(np.float32)
     nz, out = O.mhc_post_combine_norm(h, x, post, comb, w, gw, n=n, D=D, dtype="bf16", norm_eps=EPS)
     for t in range(T):
-        o = B.post_token(_bf16_val(h[t]).tolist(), _bf16_val(x[t]).tolist(), post[t].astype(np.float64).tolist(),
-                         comb[t].astype(np.float64).tolist(), n, D)
-        ob = _bf16(np.asarray(o, dtype=np.float64).astype(np.float32))
-        assert np.array_equal(ob, out[t])
-        c = B.combine_token(_bf16_val(ob).tolist(), w[t].astype(np.float64).tolist(), n, D)
-        cb = _bf16_val(_bf16(np.asarray(c).astype(np.float32)))
-        ref = B.rms_norm_row(cb.tolist(), gw.astype(np.float64).tolist(), EPS)
+        o, c = B.combine_token_f32(_bf16_val(h[t]).tolist(), _bf16_val(x[t]).tolist(), post[t].tolist(),
+                                   comb[t].tolist(), w[t].tolist(), n, D, B.bf16)
+        assert np.array_equal(_bf16_val(out[t]), np.array(o)), "fused out vs brute"
+        ref = B.rms_norm_row(c, gw.astype(np.float64).tolist(), EPS)
         assert np.array_equal(nz[t], _bf16(np.asarray(ref).astype(np.float32)))
+
+
+def pin_combine_reading_vs_float64(O):
+    """The fp32 intermediates differ from the all-float64 formulas only by storage rounding."""
+    g = np.random.default_rng(92)
+    T, n, D = 16, 4, 512
+    x = _bf16(g.standard_normal((T, n, D)))
+    h = _bf16(g.standard_normal((T, D)))
+    post = g.uniform(0, 1, (T, n)).astype(np.float32)
+    comb = O.sinkhorn(g.standard_normal((T, n, n)), 20).astype(np.float32)
+    w = g.uniform(0, 1, (T, n)).astype(np.float32)
+    gw = g.uniform(0.5, 1.5, D).astype(np.float32)
+    nz, out = O.mhc_post_combine_norm(h, x, post, comb, w, gw, n=n, D=D, dtype="bf16", norm_eps=EPS)
+    o64 = _bf16_val(O.mhc_post(h, x, post, comb, n=n, D=D, dtype="bf16"))
+    ulp_o = np.abs(_bf16_val(out) - o64) / np.maximum(np.abs(o64), 1e-30)
+    assert np.max(ulp_o) <= 2.0 ** -7 and np.mean(ulp_o > 0) < 1e-2, "post rows beyond one bf16 ulp"
+    c64 = _bf16_val(_bf16(np.einsum("tj,tjd->td", w.astype(np.float64), o64).astype(np.float32)))
+    n64 = O.rms_norm(c64, gw, EPS)
+    d = np.abs(_bf16_val(nz) - n64) / np.maximum(np.abs(n64), 1e-3 * np.sqrt(np.mean(n64 ** 2)))
+    assert np.sqrt(np.mean(d ** 2)) < 2e-3 and np.mean(d > 2.0 ** -6) < 1e-3
 
 
 ALL_PINS = [
     pin_brute_pre, pin_brute_post, pin_rounding, pin_rms_closed_form, pin_gemm_onehot_and_groups,
     pin_gates, pin_sinkhorn_exact, pin_sinkhorn_closed_forms, pin_sinkhorn_invariants,
     pin_pre_special_cases, pin_permutation_equivariance, pin_stored_outputs, pin_post_identities,
-    pin_post_orientation, pin_combine_norm,
+    pin_post_orientation, pin_combine_norm, pin_combine_reading_vs_float64,
 ]

@@ -7,7 +7,8 @@ import oracle.mhc_oracle as O
 from oracle_pins import ALL_PINS
 
 _orig = {k: getattr(O, k) for k in ("pre_logits", "gates", "sinkhorn", "post_mix", "stream_reduce",
-                                    "rms_norm", "f64_to_bf16_bits", "logit_groups", "mhc_post_combine_norm")}
+                                    "rms_norm", "f64_to_bf16_bits", "logit_groups", "mhc_post_combine_norm",
+                                    "combine_intermediates")}
 
 
 def _sinkhorn_cols_first(Z, repeat):
@@ -107,7 +108,18 @@ def _bf16_truncate(x):
     return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
+def _combine_c_unrounded(h, x, post, comb, w, dtype):
+    o, c = _orig["combine_intermediates"](h, x, post, comb, w, dtype)
+    return o, np.einsum("tj,tjd->td", np.asarray(w, dtype=np.float64), o)
+
+
+def _combine_weights_reversed(h, x, post, comb, w, dtype):
+    return _orig["combine_intermediates"](h, x, post, comb, np.asarray(w)[:, ::-1], dtype)
+
+
 MUTATIONS = {
+    "combined row kept unrounded": ("combine_intermediates", _combine_c_unrounded),
+    "combine weights applied to the wrong streams": ("combine_intermediates", _combine_weights_reversed),
     "sinkhorn columns first": ("sinkhorn", _sinkhorn_cols_first),
     "sinkhorn repeat counts half steps": ("sinkhorn", _sinkhorn_half_steps),
     "sinkhorn output transposed": ("sinkhorn", _sinkhorn_transposed),
