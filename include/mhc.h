@@ -1,0 +1,145 @@
+/*
+ * mhc.h - C ABI of the MI355X (gfx950) library for multi-stream
+ * hyper-connection (mHC) pre/post mixing.
+ *
+ * Sources, cited by page title and section:
+ *  [P1] "[sglang] AMD ROCm DeepSeek-V4 performance optimisation: Aiter MHC
+ *       kernel integration analysis" (sglang PR #24355), section 2
+ *       "DeepSeek-V4 model-layer kernel swap" (the pre call returning post,
+ *       comb and y; the post call writing into a tensor allocated like the
+ *       residual) and section 3 "TileLang kernel tuning" (the pre GEMM is a
+ *       split-K GEMM fused with a sum of squares, tiled over the hidden axis).
+ *  [P2] "[sglang] DeepSeek-V4.1 performance optimisation: mHC and metadata
+ *       overhead analysis" (sglang PR #39704), section 1 "mHC
+ *       Post/Combine/RMSNorm fusion (prefill)" and section 2 "All-reduce
+ *       kernel extension and fusion" (post mix, next-layer combine and
+ *       RMSNorm in one pass, result stored as `normalized`).
+ *
+ * Conventions shared by every entry point
+ *  - All tensors are dense, row-major (last index fastest), caller-owned
+ *    device memory. The library never allocates, frees or synchronises, and
+ *    keeps no pointer after a call returns. Calls are asynchronous on
+ *    `stream` (a hipStream_t; NULL = the default stream).
+ *  - `dt` is the storage type of the residual-shaped tensors (residual, h,
+ *    y, out, normalized). post, comb, fn, hc_scale, bias, combine_w and
+ *    norm_weight are always float32.
+ *  - Supported on the GPU: 1 <= n <= 4; D a multiple of 8 (bf16) or 4 (f32);
+ *    residual-shaped pointers 16-byte aligned; float32 pointers 4-byte
+ *    aligned. T = 0 is a successful no-op.
+ *  - Errors: argument problems return a negative status before anything is
+ *    launched, and no output is touched. A failed launch returns
+ *    MHC_ERR_HIP; mhc_last_error() then describes it. Nothing is printed and
+ *    no C++ exception crosses the boundary.
+ *  - Arithmetic: fp32 accumulation; every stored bf16 value is rounded once,
+ *    to nearest even. Results are deterministic: the same inputs and knobs
+ *    give the same bits (no floating-point atomics).
+ */
+#ifndef MHC_H_
+#define MHC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MHC_API __attribute__((visibility("default")))
+
+typedef enum {
+  MHC_OK = 0,
+  MHC_ERR_INVALID_ARG = -1,  /* null pointer, negative size, bad eps/repeat/dtype */
+  MHC_ERR_UNSUPPORTED = -2,  /* valid mathematically but not built (n > 4, D too large) */
+  MHC_ERR_MISALIGNED = -3,   /* D not a multiple of the vector width, or a pointer misaligned */
+  MHC_ERR_WORKSPACE = -4,    /* workspace missing, misaligned or smaller than required */
+  MHC_ERR_HIP = -5           /* a HIP launch failed */
+} mhc_status;
+
+typedef enum { MHC_BF16 = 0, MHC_F32 = 1 } mhc_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+MHC_API const char* mhc_status_string(int status);
+
+/* Text of the last HIP error seen by this thread (static storage, "" if none). */
+MHC_API const char* mhc_last_error(void);
+
+/* Number of split-K partials mhc_pre uses for these sizes: `n_splits` itself
+ * when positive, otherwise the library's choice for the shape. Returns a
+ * negative status for arguments mhc_pre would reject. */
+MHC_API int mhc_pre_splits(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt);
+
+/* Bytes of device workspace mhc_pre needs for these sizes and knobs (0 when
+ * T = 0; a conservative positive value for arguments it would reject is
+ * never returned - it returns 0 and mhc_pre reports the error). */
+MHC_API size_t mhc_pre_workspace_bytes(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt);
+
+/*
+ * mhc_pre - [P1] section 2 (the pre call), section 3 (split-K GEMM with sum of
+ * squares), and the closing list of [P1] (fused Sinkhorn and normalisation).
+ *
+ * For every token t, with x = residual[t] flattened stream-major
+ * (x[k] = residual[t][k / D][k % D], K = n*D) and N = n*(n+2):
+ *   r      = 1 / sqrt(sum_k x[k]^2 / K + eps)
+ *   m[c]   = sum_k x[k] * fn[k][c]                              c < N
+ *   z[c]   = hc_scale[g(c)] * (r * m[c]) + bias[c]   g = 0 (c < n), 1 (c < 2n), 2
+ *   pre[i] = sigmoid(z[i]);  post[t][i] = sigmoid(z[n + i])
+ *   comb[t] = Sinkhorn(exp(Z)), Z[i][j] = z[2n + i*n + j], `sinkhorn_repeat`
+ *            repeats of (normalise every row to sum 1, then every column)
+ *   y[t][d] = sum_i pre[i] * residual[t][i][d]
+ *
+ * Outputs (first, in the order the page's call returns them):
+ *   post  float32 [T, n]        comb float32 [T, n, n] (comb[t][i][j]: stream i -> j)
+ *   y     dt      [T, D]
+ * Inputs:
+ *   residual dt [T, n, D]; fn float32 [n*D, N]; hc_scale float32 [3]
+ *   (pre, post, comb); bias float32 [N].
+ * Knobs: sinkhorn_repeat >= 1; eps > 0; n_splits = split-K partials over the
+ *   hidden axis (0 = library choice, else 1..256; any value gives the same
+ *   result up to fp32 reassociation, and a fixed value is bitwise repeatable).
+ * Workspace: device memory of at least mhc_pre_workspace_bytes(...) bytes,
+ *   256-byte aligned, owned by the caller, not shared by concurrent calls;
+ *   its contents on entry do not matter.
+ */
+MHC_API int mhc_pre(float* post, float* comb, void* y,
+                    const void* residual, mhc_dtype dt,
+                    const float* fn, const float* hc_scale, const float* bias,
+                    int64_t T, int n, int64_t D,
+                    int sinkhorn_repeat, float eps, int n_splits,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mhc_post - [P1] section 2 (the post call, into a tensor shaped like the
+ * residual):
+ *   out[t][j][d] = post[t][j] * h[t][d] + sum_i comb[t][i][j] * residual[t][i][d]
+ * Output: out dt [T, n, D] (may not alias the inputs).
+ * Inputs: h dt [T, D] (the block output); residual dt [T, n, D];
+ *   post float32 [T, n]; comb float32 [T, n, n] as mhc_pre writes them.
+ */
+MHC_API int mhc_post(void* out, const void* h, const void* residual,
+                     const float* post, const float* comb, mhc_dtype dt,
+                     int64_t T, int n, int64_t D, void* stream);
+
+/*
+ * mhc_post_combine_norm - [P2] section 1 (post mix, combine into one bf16
+ * row, RMSNorm, one row per workgroup) and section 2 (the row is stored as
+ * `normalized`):
+ *   o_j[d]        = mhc_post result, rounded to dt
+ *   c[d]          = sum_j combine_w[t][j] * o_j[d], rounded to dt
+ *   normalized[d] = (c[d] / sqrt(sum_d c[d]^2 / D + norm_eps)) * norm_weight[d], rounded to dt
+ * Outputs: normalized dt [T, D]; out_residual dt [T, n, D] receives o (pass
+ *   NULL to skip writing it).
+ * Inputs: as mhc_post, plus combine_w float32 [T, n] and norm_weight float32
+ *   [D]; norm_eps > 0. D <= 32768 (bf16) or 16384 (f32).
+ */
+MHC_API int mhc_post_combine_norm(void* normalized, void* out_residual,
+                                  const void* h, const void* residual,
+                                  const float* post, const float* comb,
+                                  const float* combine_w, const float* norm_weight,
+                                  float norm_eps, mhc_dtype dt,
+                                  int64_t T, int n, int64_t D, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHC_H_ */

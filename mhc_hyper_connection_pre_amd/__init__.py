@@ -1,1 +1,197 @@
-"""mHC (multi-stream hyper-connection) pre/post mixing for MI355X (gfx950)."""
+"""mHC (multi-stream hyper-connection) pre/post mixing for MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``libmhc.so`` (declared in
+``include/mhc.h``). Every step of the computation runs in the library's HIP
+kernels; this module only checks tensor metadata, allocates outputs and the
+workspace with torch when the caller does not pass them, and marshals
+pointers and the current HIP stream. There is no CPU fallback: if the library
+is not built, every call raises.
+
+Functions mirror the C entry points: ``mhc_pre``, ``mhc_post``,
+``mhc_post_combine_norm``, ``mhc_pre_workspace_bytes``, ``mhc_pre_splits``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "MhcError", "lib", "library_path", "mhc_pre", "mhc_post", "mhc_post_combine_norm",
+    "mhc_pre_workspace_bytes", "mhc_pre_splits", "MHC_BF16", "MHC_F32",
+]
+
+MHC_BF16 = 0
+MHC_F32 = 1
+
+_LIB = None
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmhc.so")
+
+
+class MhcError(RuntimeError):
+    """A negative status returned by the C ABI."""
+
+    def __init__(self, fn: str, status: int):
+        L = lib()
+        msg = L.mhc_status_string(status).decode()
+        if status == -5:
+            msg += f" ({L.mhc_last_error().decode()})"
+        super().__init__(f"{fn}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load ``libmhc.so`` (once) and declare the C signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m mhc_hyper_connection_pre_amd.build` "
+                           "(there is no CPU fallback)")
+    L = ctypes.CDLL(path)
+    P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    L.mhc_status_string.argtypes = [I]
+    L.mhc_status_string.restype = ctypes.c_char_p
+    L.mhc_last_error.argtypes = []
+    L.mhc_last_error.restype = ctypes.c_char_p
+    L.mhc_pre_splits.argtypes = [I64, I, I64, I, I]
+    L.mhc_pre_splits.restype = I
+    L.mhc_pre_workspace_bytes.argtypes = [I64, I, I64, I, I]
+    L.mhc_pre_workspace_bytes.restype = SZ
+    L.mhc_pre.argtypes = [P, P, P, P, I, P, P, P, I64, I, I64, I, F, I, P, SZ, P]
+    L.mhc_pre.restype = I
+    L.mhc_post.argtypes = [P, P, P, P, P, I, I64, I, I64, P]
+    L.mhc_post.restype = I
+    L.mhc_post_combine_norm.argtypes = [P, P, P, P, P, P, P, P, F, I, I64, I, I64, P]
+    L.mhc_post_combine_norm.restype = I
+    _LIB = L
+    return L
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return MHC_BF16
+    if t.dtype == torch.float32:
+        return MHC_F32
+    raise TypeError(f"residual-shaped tensors must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t) -> int:
+    return t.data_ptr() if t is not None else None
+
+
+def _check(t, shape, dtype, device, name):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device, stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream
+
+
+def mhc_pre_splits(T: int, n: int, D: int, n_splits: int = 0, dtype_code: int = MHC_BF16) -> int:
+    st = lib().mhc_pre_splits(T, n, D, n_splits, dtype_code)
+    if st < 0:
+        raise MhcError("mhc_pre_splits", st)
+    return st
+
+
+def mhc_pre_workspace_bytes(T: int, n: int, D: int, n_splits: int = 0, dtype_code: int = MHC_BF16) -> int:
+    return lib().mhc_pre_workspace_bytes(T, n, D, n_splits, dtype_code)
+
+
+def mhc_pre(residual, fn, hc_scale, bias, *, sinkhorn_repeat: int = 20, eps: float = 1e-6, n_splits: int = 0,
+            post=None, comb=None, y=None, workspace=None, stream=None):
+    """post [T, n] f32, comb [T, n, n] f32, y [T, D] = mhc_pre(residual [T, n, D], fn, hc_scale, bias)."""
+    torch = _torch()
+    L = lib()
+    T, n, D = residual.shape
+    dev = residual.device
+    dt = _dtype_code(residual)
+    N = n * (n + 2)
+    _check(residual, (T, n, D), residual.dtype, dev, "residual")
+    _check(fn, (n * D, N), torch.float32, dev, "fn")
+    _check(hc_scale, (3,), torch.float32, dev, "hc_scale")
+    _check(bias, (N,), torch.float32, dev, "bias")
+    post = torch.empty((T, n), dtype=torch.float32, device=dev) if post is None else post
+    comb = torch.empty((T, n, n), dtype=torch.float32, device=dev) if comb is None else comb
+    y = torch.empty((T, D), dtype=residual.dtype, device=dev) if y is None else y
+    _check(post, (T, n), torch.float32, dev, "post")
+    _check(comb, (T, n, n), torch.float32, dev, "comb")
+    _check(y, (T, D), residual.dtype, dev, "y")
+    need = L.mhc_pre_workspace_bytes(T, n, D, n_splits, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    st = L.mhc_pre(_ptr(post), _ptr(comb), _ptr(y), _ptr(residual), dt, _ptr(fn), _ptr(hc_scale), _ptr(bias),
+                   T, n, D, sinkhorn_repeat, eps, n_splits, _ptr(workspace), workspace.numel(),
+                   _stream(dev, stream))
+    if st != 0:
+        raise MhcError("mhc_pre", st)
+    return post, comb, y
+
+
+def mhc_post(h, residual, post, comb, *, out=None, stream=None):
+    """out [T, n, D] = post_j * h + sum_i comb[i, j] * residual_i."""
+    torch = _torch()
+    T, n, D = residual.shape
+    dev = residual.device
+    dt = _dtype_code(residual)
+    _check(h, (T, D), residual.dtype, dev, "h")
+    _check(residual, (T, n, D), residual.dtype, dev, "residual")
+    _check(post, (T, n), torch.float32, dev, "post")
+    _check(comb, (T, n, n), torch.float32, dev, "comb")
+    out = torch.empty_like(residual) if out is None else out
+    _check(out, (T, n, D), residual.dtype, dev, "out")
+    st = lib().mhc_post(_ptr(out), _ptr(h), _ptr(residual), _ptr(post), _ptr(comb), dt, T, n, D,
+                        _stream(dev, stream))
+    if st != 0:
+        raise MhcError("mhc_post", st)
+    return out
+
+
+def mhc_post_combine_norm(h, residual, post, comb, combine_w, norm_weight, *, norm_eps: float = 1e-6,
+                          write_out: bool = True, normalized=None, out=None, stream=None):
+    """(normalized [T, D], out [T, n, D] or None): fused post mix + combine + RMSNorm."""
+    torch = _torch()
+    T, n, D = residual.shape
+    dev = residual.device
+    dt = _dtype_code(residual)
+    _check(h, (T, D), residual.dtype, dev, "h")
+    _check(residual, (T, n, D), residual.dtype, dev, "residual")
+    _check(post, (T, n), torch.float32, dev, "post")
+    _check(comb, (T, n, n), torch.float32, dev, "comb")
+    _check(combine_w, (T, n), torch.float32, dev, "combine_w")
+    _check(norm_weight, (D,), torch.float32, dev, "norm_weight")
+    normalized = torch.empty((T, D), dtype=residual.dtype, device=dev) if normalized is None else normalized
+    _check(normalized, (T, D), residual.dtype, dev, "normalized")
+    if write_out:
+        out = torch.empty_like(residual) if out is None else out
+        _check(out, (T, n, D), residual.dtype, dev, "out")
+    else:
+        out = None
+    st = lib().mhc_post_combine_norm(_ptr(normalized), _ptr(out), _ptr(h), _ptr(residual), _ptr(post), _ptr(comb),
+                                     _ptr(combine_w), _ptr(norm_weight), norm_eps, dt, T, n, D,
+                                     _stream(dev, stream))
+    if st != 0:
+        raise MhcError("mhc_post_combine_norm", st)
+    return normalized, out

@@ -1,0 +1,189 @@
+// C ABI of the mHC library: argument validation, split-K planning, launches.
+// Every check runs before the first HIP call, so a rejected call launches
+// nothing and touches no output.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+
+#include "mhc_internal.h"
+
+namespace mhc {
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int hip_fail(hipError_t e) {
+  std::snprintf(g_last_error, sizeof g_last_error, "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+  return MHC_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int vec_elems(mhc_dtype dt) { return dt == MHC_BF16 ? 8 : 4; }
+
+size_t elem_bytes(mhc_dtype dt) { return dt == MHC_BF16 ? 2 : 4; }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Shape checks shared by every entry point.
+int check_shape(int64_t T, int n, int64_t D, mhc_dtype dt) {
+  if (dt != MHC_BF16 && dt != MHC_F32) return MHC_ERR_INVALID_ARG;
+  if (T < 0 || n < 1 || D < 1) return MHC_ERR_INVALID_ARG;
+  if (n > 4) return MHC_ERR_UNSUPPORTED;
+  if (D % vec_elems(dt) != 0) return MHC_ERR_MISALIGNED;
+  // grid.x is the token count; keep every byte offset far from int64 overflow
+  if (T > 0x7fffffffLL || D > (1LL << 26)) return MHC_ERR_UNSUPPORTED;
+  return MHC_OK;
+}
+
+}  // namespace
+
+int make_pre_plan(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, PrePlan* p) {
+  int st = check_shape(T, n, D, dt);
+  if (st != MHC_OK) return st;
+  if (n_splits < 0 || n_splits > 256) return MHC_ERR_INVALID_ARG;
+  PrePlan q{};
+  q.T = T;
+  q.D = D;
+  q.n = n;
+  q.K = (int64_t)n * D;
+  q.N = n * (n + 2);
+  q.NP = (q.N + 1 + 3) / 4 * 4;
+  q.dt = dt;
+  // One "k-step" is 32 hidden elements for the MFMA path, 64 for the VALU path.
+  const int kstep = dt == MHC_BF16 ? 32 : 64;
+  q.ksteps = (int)((q.K + kstep - 1) / kstep);
+  if (dt == MHC_BF16) {
+    q.NCB = (2 * q.N + 15) / 16;
+    if (n_splits == 1) {  // one split: a tall workgroup of 16 waves per 16 tokens keeps the k-loop parallel
+      q.MT = 1;
+      q.NW = 16;
+    } else {
+      q.MT = 4;
+      q.NW = 4;
+    }
+    q.tok_per_wg = 16 * q.MT;
+  } else {
+    q.NCB = 0;
+    q.MT = 0;
+    q.NW = 1;
+    q.tok_per_wg = 4;
+  }
+  const int64_t groups = T > 0 ? (T + q.tok_per_wg - 1) / q.tok_per_wg : 1;
+  int S = n_splits;
+  if (S == 0) {
+    // Library choice: about 512 workgroups, each split at least one k-step per wave.
+    int64_t want = (512 + groups - 1) / groups;
+    int64_t cap = q.ksteps / q.NW;
+    if (cap < 1) cap = 1;
+    if (cap > 64) cap = 64;
+    S = (int)(want < 1 ? 1 : (want > cap ? cap : want));
+  }
+  if (S > q.ksteps) S = q.ksteps;
+  q.steps_per_split = (q.ksteps + S - 1) / S;
+  q.S = (q.ksteps + q.steps_per_split - 1) / q.steps_per_split;  // no empty split
+  q.off_fnp = 0;
+  q.fnp_bytes = dt == MHC_BF16 ? (size_t)q.ksteps * q.NCB * 64 * 16 : 0;
+  q.off_part = align_up(q.fnp_bytes, 256);
+  q.part_bytes = (size_t)q.S * (size_t)T * q.NP * sizeof(float);
+  q.total_bytes = align_up(q.off_part + q.part_bytes, 256);
+  *p = q;
+  return MHC_OK;
+}
+
+}  // namespace mhc
+
+using namespace mhc;
+
+extern "C" {
+
+MHC_API const char* mhc_status_string(int status) {
+  switch (status) {
+    case MHC_OK: return "MHC_OK";
+    case MHC_ERR_INVALID_ARG: return "MHC_ERR_INVALID_ARG: null pointer, negative size or invalid knob";
+    case MHC_ERR_UNSUPPORTED: return "MHC_ERR_UNSUPPORTED: shape not supported by the GPU kernels";
+    case MHC_ERR_MISALIGNED: return "MHC_ERR_MISALIGNED: D not a multiple of the vector width, or pointer misaligned";
+    case MHC_ERR_WORKSPACE: return "MHC_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case MHC_ERR_HIP: return "MHC_ERR_HIP: a HIP launch failed (see mhc_last_error)";
+    default: return "unknown mhc status";
+  }
+}
+
+MHC_API const char* mhc_last_error(void) { return g_last_error; }
+
+MHC_API int mhc_pre_splits(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt) {
+  PrePlan p;
+  const int st = make_pre_plan(T, n, D, n_splits, dt, &p);
+  return st != MHC_OK ? st : p.S;
+}
+
+MHC_API size_t mhc_pre_workspace_bytes(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt) {
+  PrePlan p;
+  if (T == 0 || make_pre_plan(T, n, D, n_splits, dt, &p) != MHC_OK) return 0;
+  return p.total_bytes;
+}
+
+MHC_API int mhc_pre(float* post, float* comb, void* y, const void* residual, mhc_dtype dt, const float* fn,
+                    const float* hc_scale, const float* bias, int64_t T, int n, int64_t D, int sinkhorn_repeat,
+                    float eps, int n_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  PrePlan p;
+  int st = make_pre_plan(T, n, D, n_splits, dt, &p);
+  if (st != MHC_OK) return st;
+  if (sinkhorn_repeat < 1 || !(eps > 0.0f) || !std::isfinite(eps)) return MHC_ERR_INVALID_ARG;
+  if (T == 0) return MHC_OK;
+  if (!post || !comb || !y || !residual || !fn || !hc_scale || !bias) return MHC_ERR_INVALID_ARG;
+  if (!aligned(y, 16) || !aligned(residual, 16)) return MHC_ERR_MISALIGNED;
+  if (!aligned(post, 4) || !aligned(comb, 4) || !aligned(fn, 4) || !aligned(hc_scale, 4) || !aligned(bias, 4))
+    return MHC_ERR_MISALIGNED;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.total_bytes) return MHC_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* part = reinterpret_cast<float*>(ws + p.off_part);
+  void* fnp = ws + p.off_fnp;
+  hipError_t e;
+  if (dt == MHC_BF16) {
+    e = launch_pack_fn(p, fn, fnp, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  e = launch_pre_gemm(p, residual, fnp, fn, part, s);
+  if (e != hipSuccess) return hip_fail(e);
+  e = launch_pre_epilogue(p, residual, part, hc_scale, bias, post, comb, y, sinkhorn_repeat, eps, s);
+  if (e != hipSuccess) return hip_fail(e);
+  return MHC_OK;
+}
+
+MHC_API int mhc_post(void* out, const void* h, const void* residual, const float* post, const float* comb,
+                     mhc_dtype dt, int64_t T, int n, int64_t D, void* stream) {
+  int st = check_shape(T, n, D, dt);
+  if (st != MHC_OK) return st;
+  if (T == 0) return MHC_OK;
+  if (!out || !h || !residual || !post || !comb) return MHC_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(h, 16) || !aligned(residual, 16)) return MHC_ERR_MISALIGNED;
+  if (!aligned(post, 4) || !aligned(comb, 4)) return MHC_ERR_MISALIGNED;
+  const hipError_t e = launch_post(h, residual, post, comb, out, dt, T, n, D, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MHC_OK : hip_fail(e);
+}
+
+MHC_API int mhc_post_combine_norm(void* normalized, void* out_residual, const void* h, const void* residual,
+                                  const float* post, const float* comb, const float* combine_w,
+                                  const float* norm_weight, float norm_eps, mhc_dtype dt, int64_t T, int n,
+                                  int64_t D, void* stream) {
+  int st = check_shape(T, n, D, dt);
+  if (st != MHC_OK) return st;
+  if (!(norm_eps > 0.0f) || !std::isfinite(norm_eps)) return MHC_ERR_INVALID_ARG;
+  if (D / vec_elems(dt) > kPcnMaxVectors) return MHC_ERR_UNSUPPORTED;
+  if (T == 0) return MHC_OK;
+  if (!normalized || !h || !residual || !post || !comb || !combine_w || !norm_weight) return MHC_ERR_INVALID_ARG;
+  if (!aligned(normalized, 16) || !aligned(h, 16) || !aligned(residual, 16) ||
+      (out_residual && !aligned(out_residual, 16)))
+    return MHC_ERR_MISALIGNED;
+  if (!aligned(post, 4) || !aligned(comb, 4) || !aligned(combine_w, 4) || !aligned(norm_weight, 4))
+    return MHC_ERR_MISALIGNED;
+  const hipError_t e = launch_post_combine_norm(normalized, out_residual, h, residual, post, comb, combine_w,
+                                                norm_weight, norm_eps, dt, T, n, D, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MHC_OK : hip_fail(e);
+}
+
+}  // extern "C"

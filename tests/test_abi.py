@@ -1,0 +1,138 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared
+symbol, and rejects bad arguments before any HIP call (so nothing launches)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import mhc_hyper_connection_pre_amd as mhc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mhc.h")
+
+OK, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE = 0, -1, -2, -3, -4
+BF16, F32 = 0, 1
+A = 0x100000          # a fake, 256-byte aligned "device" address: never dereferenced here
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"MHC_API\s+[\w\s\*]+?\b(mhc_\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mhc.library_path()):
+        pytest.skip("libmhc.so not built")
+    return mhc.lib()
+
+
+def test_header_declares_the_boundary():
+    syms = set(declared_symbols())
+    assert {"mhc_pre", "mhc_post", "mhc_post_combine_norm", "mhc_pre_workspace_bytes",
+            "mhc_pre_splits", "mhc_status_string", "mhc_last_error"} <= syms
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", mhc.library_path()], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)$", out, flags=re.M))
+    for s in declared_symbols():
+        assert s in exported, f"{s} declared in include/mhc.h but not exported"
+        assert hasattr(L, s)
+    # nothing but the C ABI is exported from the library's own code
+    assert not [s for s in exported if s.startswith("_ZN3mhc")]
+
+
+def test_status_strings(L):
+    for st in (OK, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE, -5):
+        assert L.mhc_status_string(st).decode().startswith("MHC_")
+    assert L.mhc_status_string(42) == b"unknown mhc status"
+    assert L.mhc_last_error() == b""
+
+
+def pre(L, T=16, n=4, D=64, dt=BF16, post=A, comb=A, y=A, res=A, fn=A, hc=A, bias=A, repeat=20, eps=1e-6,
+        splits=0, ws=A, ws_bytes=1 << 30):
+    return L.mhc_pre(post, comb, y, res, dt, fn, hc, bias, T, n, D, repeat, eps, splits, ws, ws_bytes, None)
+
+
+def test_pre_validation(L):
+    assert pre(L, T=0) == OK                       # no-op, nothing launched
+    assert pre(L, T=0, post=None, y=None) == OK
+    assert pre(L, T=-1) == INVALID
+    assert pre(L, n=0) == INVALID
+    assert pre(L, n=5) == UNSUPPORTED
+    assert pre(L, D=0) == INVALID
+    assert pre(L, D=12) == MISALIGNED               # bf16 needs D % 8 == 0
+    assert pre(L, D=12, dt=F32, T=0) == OK          # f32 needs D % 4 == 0
+    assert pre(L, dt=7) == INVALID
+    assert pre(L, repeat=0) == INVALID
+    assert pre(L, eps=0.0) == INVALID
+    assert pre(L, eps=float("nan")) == INVALID
+    assert pre(L, splits=-1) == INVALID
+    assert pre(L, splits=257) == INVALID
+    for k in ("post", "comb", "y", "res", "fn", "hc", "bias"):
+        assert pre(L, **{k: None}) == INVALID, k
+    assert pre(L, y=A + 8) == MISALIGNED
+    assert pre(L, res=A + 2) == MISALIGNED
+    assert pre(L, post=A + 2) == MISALIGNED
+    assert pre(L, ws=None) == WORKSPACE
+    assert pre(L, ws=A + 16) == WORKSPACE
+    need = L.mhc_pre_workspace_bytes(16, 4, 64, 0, BF16)
+    assert need > 0
+    assert pre(L, ws_bytes=need - 1) == WORKSPACE
+
+
+def test_pre_plan(L):
+    # split count: explicit values honoured (capped at the number of 32-wide k-steps), auto is positive
+    assert L.mhc_pre_splits(2048, 4, 4096, 1, BF16) == 1
+    assert L.mhc_pre_splits(16384, 4, 7168, 4, BF16) == 4
+    assert L.mhc_pre_splits(16384, 4, 7168, 8, BF16) == 8
+    assert L.mhc_pre_splits(2048, 4, 7168, 0, BF16) >= 1
+    assert L.mhc_pre_splits(1, 1, 8, 64, BF16) == 1              # K = 8: one k-step
+    assert L.mhc_pre_splits(1, 5, 8, 0, BF16) == UNSUPPORTED
+    assert L.mhc_pre_workspace_bytes(0, 4, 64, 0, BF16) == 0
+    assert L.mhc_pre_workspace_bytes(16, 5, 64, 0, BF16) == 0
+    # workspace: packed fn (K/32 x 3 column blocks x 1 KiB) + partials [S, T, 28] fp32, 256-aligned
+    T, n, D = 2048, 4, 7168
+    S = L.mhc_pre_splits(T, n, D, 0, BF16)
+    ws = L.mhc_pre_workspace_bytes(T, n, D, 0, BF16)
+    fnp = (n * D // 32) * 3 * 1024
+    part = S * T * 28 * 4
+    assert ws == (fnp + 255) // 256 * 256 + (part + 255) // 256 * 256 or ws >= fnp + part
+    assert L.mhc_pre_workspace_bytes(8, 4, 256, 0, F32) == (L.mhc_pre_splits(8, 4, 256, 0, F32) * 8 * 28 * 4 + 255) // 256 * 256
+
+
+def test_post_validation(L):
+    def post(T=4, n=4, D=64, dt=BF16, out=A, h=A, res=A, p=A, c=A):
+        return L.mhc_post(out, h, res, p, c, dt, T, n, D, None)
+    assert post(T=0) == OK
+    assert post(T=-3) == INVALID
+    assert post(n=5) == UNSUPPORTED
+    assert post(D=4) == MISALIGNED
+    assert post(out=None) == INVALID
+    assert post(h=A + 4) == MISALIGNED
+    assert post(c=A + 1) == MISALIGNED
+
+
+def test_post_combine_norm_validation(L):
+    def pcn(T=4, n=4, D=64, dt=BF16, nz=A, out=A, h=A, res=A, p=A, c=A, w=A, g=A, eps=1e-6):
+        return L.mhc_post_combine_norm(nz, out, h, res, p, c, w, g, eps, dt, T, n, D, None)
+    assert pcn(T=0) == OK
+    assert pcn(T=0, out=None) == OK
+    assert pcn(eps=0.0) == INVALID
+    assert pcn(nz=None) == INVALID
+    assert pcn(w=None) == INVALID
+    assert pcn(out=A + 8) == MISALIGNED
+    assert pcn(D=8 * 4097) == UNSUPPORTED          # more than 1024 threads x 4 vectors
+    assert pcn(D=8 * 4096, T=0) == OK
+
+
+def test_binding_raises_without_gpu_tensors(L):
+    import torch
+    x = torch.zeros((2, 4, 8), dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        mhc.mhc_post(x[:, 0].float(), x, torch.zeros(2, 4), torch.zeros(2, 4, 4))

@@ -1,0 +1,262 @@
+"""HIP path vs the float64 oracle on the same seeded inputs (needs an MI355X).
+
+Small shapes span several tiles and a ragged tail and are compared element by
+element; the named workloads run at full size in the launch configuration the
+benchmark times, compared in full where the oracle finishes in seconds and on
+sampled tokens for the 16384-token prefill.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import mhc_hyper_connection_pre_amd as mhc
+from mhc_hyper_connection_pre_amd import workloads as W
+import oracle.mhc_oracle as O
+from parity import assert_close, dev_tensor, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _gpu_inputs(x):
+    d = {k: dev_tensor(v) for k, v in x.arrays().items()}
+    return d
+
+
+def _oracle_pre(x, tokens=None):
+    s = x.spec
+    res = x.residual if tokens is None else x.residual[tokens]
+    return O.mhc_pre(res, x.fn, x.hc_scale, x.bias, n=s.n, D=s.D, dtype=s.dtype,
+                     sinkhorn_repeat=s.sinkhorn_repeat, eps=s.eps)
+
+
+def _check_pre(x, g, n_splits, tokens=None, what=""):
+    s = x.spec
+    post, comb, y = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], sinkhorn_repeat=s.sinkhorn_repeat,
+                                eps=s.eps, n_splits=n_splits)
+    torch.cuda.synchronize()
+    hp, hc, hy = host(post), host(comb), host(y)
+    if tokens is not None:
+        hp, hc, hy = hp[tokens], hc[tokens], hy[tokens]
+    op, oc, oy = _oracle_pre(x, tokens)
+    e1 = assert_close(hp, op, "gate", f"{what} post")
+    e2 = assert_close(hc, oc, "gate", f"{what} comb")
+    e3 = assert_close(hy, oy, "tensor", f"{what} y")
+    _say(f"  {what}: post {e1:.2e} comb {e2:.2e} y {e3:.2e}")
+    return post, comb, y
+
+
+def _check_post(x, g, post_np, comb_np, tokens=None, what=""):
+    s = x.spec
+    out = mhc.mhc_post(g["h"], g["residual"], dev_tensor(post_np), dev_tensor(comb_np))
+    torch.cuda.synchronize()
+    ho = host(out)
+    if tokens is not None:
+        ho = ho[tokens]
+        want = O.mhc_post(x.h[tokens], x.residual[tokens], post_np[tokens], comb_np[tokens], n=s.n, D=s.D,
+                          dtype=s.dtype)
+    else:
+        want = O.mhc_post(x.h, x.residual, post_np, comb_np, n=s.n, D=s.D, dtype=s.dtype)
+    e = assert_close(ho, want, "tensor", f"{what} out")
+    _say(f"  {what}: out {e:.2e}")
+    return out
+
+
+# ---------------------------------------------------------------- small, ragged, every n and dtype
+
+SMALL = [(T, n, D, dt, sp) for (T, n, D) in ((1, 4, 8), (7, 4, 264), (33, 4, 1032), (67, 3, 520),
+                                             (130, 2, 2056), (17, 1, 72), (5, 4, 4104))
+         for dt in ("bf16", "f32") for sp in (0, 1, 3)]
+
+
+@pytest.mark.parametrize("T,n,D,dt,sp", SMALL, ids=lambda v: str(v))
+def test_small_pre_post(T, n, D, dt, sp):
+    if dt == "f32" and D % 4:
+        pytest.skip("f32 needs D % 4 == 0")
+    x = W.generate(W.custom(T, n, D, dt, seed=T * 131 + n * 7 + D, fn_std=0.05))
+    g = _gpu_inputs(x)
+    post, comb, y = _check_pre(x, g, sp, what=f"T{T} n{n} D{D} {dt} S{sp}")
+    op, oc, _ = _oracle_pre(x)
+    _check_post(x, g, op, oc, what=f"T{T} n{n} D{D} {dt}")
+
+
+@pytest.mark.parametrize("T,n,D,dt", [(3, 4, 64, "bf16"), (65, 4, 5120, "bf16"), (9, 2, 1024, "f32"),
+                                      (4, 1, 32768, "bf16"), (2, 4, 16384, "f32")])
+def test_small_post_combine_norm(T, n, D, dt):
+    x = W.generate(W.custom(T, n, D, dt, seed=5 + T + D, combine=True))
+    g = _gpu_inputs(x)
+    op, oc, _ = _oracle_pre(x)
+    want_nz, want_out = O.mhc_post_combine_norm(x.h, x.residual, op, oc, x.combine_w, x.norm_weight, n=n, D=D,
+                                                dtype=dt, norm_eps=x.spec.norm_eps)
+    for write_out in (True, False):
+        nz, out = mhc.mhc_post_combine_norm(g["h"], g["residual"], dev_tensor(op), dev_tensor(oc), g["combine_w"],
+                                            g["norm_weight"], norm_eps=x.spec.norm_eps, write_out=write_out)
+        torch.cuda.synchronize()
+        assert_close(host(nz), want_nz, "tensor", "normalized")
+        if write_out:
+            assert_close(host(out), want_out, "tensor", "out")
+
+
+# ---------------------------------------------------------------- named workloads at full size
+
+def test_tiny_f32_workload():
+    x = W.generate(W.spec("tiny-f32"))
+    s = x.spec
+    g = _gpu_inputs(x)
+    post, comb, y = _check_pre(x, g, s.n_splits, what="tiny-f32")
+    c = host(comb).astype(np.float64)
+    assert np.all(c >= 0)
+    assert np.max(np.abs(c.sum(axis=1) - 1)) <= 1e-5
+    assert np.max(np.abs(c.sum(axis=2) - 1)) <= 1e-4
+    op, oc, _ = _oracle_pre(x)
+    _check_post(x, g, op, oc, what="tiny-f32")
+    want_nz, want_out = O.mhc_post_combine_norm(x.h, x.residual, op, oc, x.combine_w, x.norm_weight, n=s.n, D=s.D,
+                                                dtype=s.dtype, norm_eps=s.norm_eps)
+    nz, out = mhc.mhc_post_combine_norm(g["h"], g["residual"], dev_tensor(op), dev_tensor(oc), g["combine_w"],
+                                        g["norm_weight"], norm_eps=s.norm_eps)
+    torch.cuda.synchronize()
+    assert_close(host(nz), want_nz, "tensor", "tiny normalized")
+    assert_close(host(out), want_out, "tensor", "tiny out")
+
+
+@pytest.mark.parametrize("name", ["prefill-d4096", "prefill-d7168"])
+def test_prefill_workload_full(name):
+    x = W.generate(W.spec(name))
+    s = x.spec
+    g = _gpu_inputs(x)
+    post, comb, y = _check_pre(x, g, s.n_splits, what=name)
+    c = host(comb).astype(np.float64)
+    assert np.all(c >= 0) and np.max(np.abs(c.sum(axis=1) - 1)) <= 1e-5
+    # post on the GPU's own post/comb (the benchmark's chain) and on the oracle's
+    _check_post(x, g, host(post), host(comb), what=f"{name} chained")
+
+
+@pytest.mark.parametrize("name", ["decode-t32-d5120", "decode-t64-d5120"])
+def test_decode_workload(name):
+    x = W.generate(W.spec(name))
+    s = x.spec
+    g = _gpu_inputs(x)
+    _check_pre(x, g, s.n_splits, what=name)
+    op, oc, _ = _oracle_pre(x)
+    _check_post(x, g, op, oc, what=name)
+    want_nz, want_out = O.mhc_post_combine_norm(x.h, x.residual, op, oc, x.combine_w, x.norm_weight, n=s.n, D=s.D,
+                                                dtype=s.dtype, norm_eps=s.norm_eps)
+    for write_out in (True, False):
+        nz, out = mhc.mhc_post_combine_norm(g["h"], g["residual"], dev_tensor(op), dev_tensor(oc), g["combine_w"],
+                                            g["norm_weight"], norm_eps=s.norm_eps, write_out=write_out)
+        torch.cuda.synchronize()
+        e = assert_close(host(nz), want_nz, "tensor", f"{name} normalized")
+        if write_out:
+            assert_close(host(out), want_out, "tensor", f"{name} out")
+        _say(f"  {name} fused (out={write_out}): normalized {e:.2e}")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("n_splits", [4, 2, 8])
+def test_large_prefill_sampled(n_splits):
+    s = W.spec("prefill-t16384-d7168", n_splits=n_splits)
+    x = W.generate(s)
+    g = _gpu_inputs(x)
+    rng = np.random.default_rng(99)
+    tokens = np.unique(np.concatenate([[0, 1, s.T - 1], rng.choice(s.T, 125, replace=False)]))
+    post, comb, y = _check_pre(x, g, n_splits, tokens=tokens, what=f"T16384 S{n_splits}")
+    op, oc, _ = _oracle_pre(x, tokens)
+    full_post, full_comb = host(post), host(comb)
+    # post on GPU post/comb, checked on the sampled tokens (the oracle takes the GPU's fp32 gates as stored)
+    out = mhc.mhc_post(g["h"], g["residual"], post, comb)
+    torch.cuda.synchronize()
+    want = O.mhc_post(x.h[tokens], x.residual[tokens], full_post[tokens], full_comb[tokens], n=s.n, D=s.D,
+                      dtype=s.dtype)
+    assert_close(host(out)[tokens], want, "tensor", "T16384 out")
+    # properties that hold at every token
+    c = full_comb.astype(np.float64)
+    assert np.all(c >= 0) and np.max(np.abs(c.sum(axis=1) - 1)) <= 1e-5
+    assert np.all((full_post > 0) & (full_post < 1))
+    del g, out, y
+
+
+# ---------------------------------------------------------------- invariants, determinism, edges
+
+def test_identity_post_is_exact():
+    for dt in ("bf16", "f32"):
+        x = W.generate(W.custom(37, 4, 1032, dt, seed=3))
+        g = _gpu_inputs(x)
+        T, n = 37, 4
+        eye = torch.eye(n, device="cuda").expand(T, n, n).contiguous()
+        out = mhc.mhc_post(g["h"], g["residual"], torch.zeros(T, n, device="cuda"), eye)
+        assert torch.equal(out.view(torch.int16) if dt == "bf16" else out,
+                           g["residual"].view(torch.int16) if dt == "bf16" else g["residual"])
+        out = mhc.mhc_post(g["h"], g["residual"], torch.ones(T, n, device="cuda"),
+                           torch.zeros(T, n, n, device="cuda"))
+        assert torch.equal(out, g["h"][:, None, :].expand(T, n, -1))
+
+
+def test_n1_is_gated_rms_scaled_copy():
+    x = W.generate(W.custom(9, 1, 2048, "bf16", seed=4))
+    g = _gpu_inputs(x)
+    post, comb, y = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(comb.cpu(), torch.ones(9, 1, 1))
+    _, _, _, it = O.mhc_pre(x.residual, x.fn, x.hc_scale, x.bias, n=1, D=2048, dtype="bf16", sinkhorn_repeat=20,
+                            eps=1e-6, intermediates=True)
+    ref = it["pre"][:, 0:1] * O.decode(x.residual, "bf16")[:, 0, :]
+    assert_close(host(y), O.encode(ref, "bf16"), "tensor", "n=1 y")
+
+
+def test_split_invariance_and_determinism():
+    x = W.generate(W.custom(300, 4, 7168, "bf16", seed=8))
+    g = _gpu_inputs(x)
+    res = {}
+    for sp in (1, 2, 4, 8, 0):
+        a = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], n_splits=sp)
+        b = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], n_splits=sp)
+        torch.cuda.synchronize()
+        for u, v in zip(a, b):
+            assert torch.equal(u.view(torch.int16) if u.dtype == torch.bfloat16 else u,
+                               v.view(torch.int16) if v.dtype == torch.bfloat16 else v), f"repeat differs S={sp}"
+        res[sp] = [host(t) for t in a]
+    for sp in (2, 4, 8, 0):
+        for k in (0, 1):
+            d = np.max(np.abs(res[sp][k].astype(np.float64) - res[1][k]) / np.maximum(np.abs(res[1][k]), 1e-6))
+            assert d <= 1e-4, (sp, k, d)
+
+
+def test_outputs_fully_written_and_bounded():
+    """NaN-prefilled outputs are overwritten everywhere; canaries past the end are untouched."""
+    T, n, D = 45, 4, 1544
+    x = W.generate(W.custom(T, n, D, "bf16", seed=12))
+    g = _gpu_inputs(x)
+    pad = 64
+    post_b = torch.full((T * n + pad,), float("nan"), device="cuda")
+    comb_b = torch.full((T * n * n + pad,), float("nan"), device="cuda")
+    y_b = torch.full((T * D + pad,), float("nan"), device="cuda", dtype=torch.bfloat16)
+    out_b = torch.full((T * n * D + pad,), float("nan"), device="cuda", dtype=torch.bfloat16)
+    post, comb, y = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], post=post_b[:T * n].view(T, n),
+                                comb=comb_b[:T * n * n].view(T, n, n), y=y_b[:T * D].view(T, D))
+    out = mhc.mhc_post(g["h"], g["residual"], post, comb, out=out_b[:T * n * D].view(T, n, D))
+    torch.cuda.synchronize()
+    for full, used in ((post_b, T * n), (comb_b, T * n * n), (y_b, T * D), (out_b, T * n * D)):
+        assert not torch.isnan(full[:used]).any()
+        assert torch.isnan(full[used:]).all()
+
+
+def test_error_paths_on_gpu():
+    x = W.generate(W.custom(8, 4, 64, "bf16", seed=2))
+    g = _gpu_inputs(x)
+    big = torch.empty(8 * 4 * 64 + 8, dtype=torch.bfloat16, device="cuda")
+    mis = big[1:1 + 8 * 4 * 64].view(8, 4, 64)
+    with pytest.raises(mhc.MhcError) as e:
+        mhc.mhc_pre(mis, g["fn"], g["hc_scale"], g["bias"])
+    assert e.value.status == -3
+    with pytest.raises(mhc.MhcError) as e:
+        mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"],
+                    workspace=torch.empty(256, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == -4
+    # T = 0 is a no-op
+    z = torch.empty((0, 4, 64), dtype=torch.bfloat16, device="cuda")
+    p, c, y = mhc.mhc_pre(z, g["fn"], g["hc_scale"], g["bias"])
+    assert p.shape == (0, 4) and y.shape == (0, 64)
