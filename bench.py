@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the mHC layer-boundary hot path on one MI355X.
+
+One step = mhc_pre on a [T, n, D] residual followed by mhc_post on the same
+residual with the block output h, using the post/comb that pre produced. The
+default workload is prefill with T = 2048 tokens, n = 4 streams, D = 7168
+(bf16), fn fp32 [28672, 24]. Inputs are seeded synthetic data already
+resident in HBM when the timed region starts. Steps rotate over several input
+and output buffer sets so that no step reads data the previous step left in
+the 256 MB Infinity Cache.
+
+Prints one JSON line: tokens/s (value), algorithmic HBM GB/s and its fraction
+of the 8 TB/s peak, a roofline object for the dominant kernel (algorithmic
+bytes per launch / average launch duration from HIP events recorded on the
+launch stream), and the CPU oracle timed on the host as a baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       python bench.py --summarize-rocprof DIR   (summarise rocprofv3 output)
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "mhc_pre+post tokens/s and HBM GB/s (% of peak), T=2048 n=4 D=7168"
+PEAK_HBM_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic_post_prefill-d7168.txt")
+POST_SOURCE = os.path.join(ROOT, "mhc_hyper_connection_pre_amd", "csrc", "mhc_post.hip")
+
+
+# ---------------------------------------------------------------- algorithmic bytes
+
+def pre_bytes(T, n, D, e):
+    """Every input read once, every output written once: residual, fn, hc_scale + bias, y, post + comb."""
+    N = n * (n + 2)
+    return T * n * D * e + n * D * N * 4 + (N + 3) * 4 + T * D * e + T * (n + n * n) * 4
+
+
+def post_bytes(T, n, D, e):
+    """h, residual, post + comb read once; out written once."""
+    return T * D * e + T * n * D * e + T * (n + n * n) * 4 + T * n * D * e
+
+
+# ---------------------------------------------------------------- traffic from counters
+
+def source_hash(path=POST_SOURCE):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic():
+    """Counter-derived HBM bytes per post launch, if measured on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize_rocprof(d):
+    """Print per-kernel averages from a rocprofv3 output directory (kernel trace and/or counters)."""
+    rows = {}
+    for path in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            rows.setdefault(r["Name"], {}).update(
+                {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+                 "total_us": float(r["TotalDurationNs"]) / 1e3, "pct": float(r["Percentage"])})
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            key = (r["Kernel_Name"], r["Counter_Name"])
+            acc.setdefault(key, []).append(float(r["Counter_Value"]))
+        for (k, c), v in acc.items():
+            rows.setdefault(k, {})[c + "_avg"] = sum(v) / len(v)
+            rows.setdefault(k, {})[c + "_n"] = len(v)
+    for k, v in sorted(rows.items(), key=lambda kv: -kv[1].get("total_us", 0)):
+        print(json.dumps({"kernel": k, **v}))
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(x, min_seconds):
+    """The float64 oracle (as it stands) on the same workload, repeated until min_seconds elapse."""
+    import numpy as np
+    import oracle.mhc_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report one thread per BLAS call
+        blas = 1
+    s = x.spec
+    reps, t_total = 0, 0.0
+    while t_total < min_seconds or reps == 0:
+        t0 = time.perf_counter()
+        post, comb, y = O.mhc_pre(x.residual, x.fn, x.hc_scale, x.bias, n=s.n, D=s.D, dtype=s.dtype,
+                                  sinkhorn_repeat=s.sinkhorn_repeat, eps=s.eps)
+        O.mhc_post(x.h, x.residual, post, comb, n=s.n, D=s.D, dtype=s.dtype)
+        t_total += time.perf_counter() - t0
+        reps += 1
+        if reps >= 20:
+            break
+    del np
+    return {"value": reps * s.T / t_total, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
+            "sample": f"full workload ({s.T} tokens) x {reps} repetition(s), {t_total:.1f} s; float64 numpy, "
+                      f"matmul on {blas} BLAS thread(s), elementwise single-threaded",
+            "host_cpus_available": len(os.sched_getaffinity(0))}
+
+
+# ---------------------------------------------------------------- GPU benchmark
+
+def run(args):
+    import numpy as np
+    import torch
+
+    import mhc_hyper_connection_pre_amd as mhc
+    from mhc_hyper_connection_pre_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU (torch.cuda.is_available() is False)")
+    dev = torch.device("cuda:0")
+    spec = W.spec(args.workload)
+    if args.n_splits is not None:
+        spec = W.spec(args.workload, n_splits=args.n_splits)
+    x = W.generate(spec)
+    T, n, D = spec.T, spec.n, spec.D
+    tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+    e = 2 if spec.dtype == "bf16" else 4
+
+    def dev_t(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    fn, hc, bias = dev_t(x.fn), dev_t(x.hc_scale), dev_t(x.bias)
+    per_set = pre_bytes(T, n, D, e) + post_bytes(T, n, D, e)
+    nsets = max(2, min(8, int(3 * 256e6 // max(per_set, 1)) + 1))
+    sets = []
+    for k in range(nsets):
+        res = dev_t(x.residual) if k == 0 else sets[0]["residual"].clone()
+        h = dev_t(x.h) if k == 0 else sets[0]["h"].clone()
+        sets.append({
+            "residual": res, "h": h,
+            "post": torch.empty((T, n), dtype=torch.float32, device=dev),
+            "comb": torch.empty((T, n, n), dtype=torch.float32, device=dev),
+            "y": torch.empty((T, D), dtype=tdt, device=dev),
+            "out": torch.empty((T, n, D), dtype=tdt, device=dev),
+        })
+    ws_bytes = mhc.mhc_pre_workspace_bytes(T, n, D, spec.n_splits, 0 if spec.dtype == "bf16" else 1)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    S = mhc.mhc_pre_splits(T, n, D, spec.n_splits, 0 if spec.dtype == "bf16" else 1)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(b, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mhc.mhc_pre(b["residual"], fn, hc, bias, sinkhorn_repeat=spec.sinkhorn_repeat, eps=spec.eps,
+                    n_splits=spec.n_splits, post=b["post"], comb=b["comb"], y=b["y"], workspace=ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        mhc.mhc_post(b["h"], b["residual"], b["post"], b["comb"], out=b["out"], stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % nsets], events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    pre_ms = sum(ev[0].elapsed_time(ev[1]) for ev in events) / args.steps
+    post_ms = sum(ev[1].elapsed_time(ev[2]) for ev in events) / args.steps
+
+    bp, bq = pre_bytes(T, n, D, e), post_bytes(T, n, D, e)
+    step_gbps = (bp + bq) / (ms_per_step * 1e-3) / 1e9
+    post_gbps = bq / (post_ms * 1e-3) / 1e9
+    pre_gbps = bp / (pre_ms * 1e-3) / 1e9
+    traffic = stored_traffic() if args.workload == W.THROUGHPUT_WORKLOAD else None
+    result = {
+        "metric": METRIC,
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if spec.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "T": T, "n": n, "D": D, "n_splits": S,
+                   "sinkhorn_repeat": spec.sinkhorn_repeat, "buffer_sets": nsets},
+        "hbm_gbps": step_gbps,
+        "hbm_frac_of_peak": step_gbps / PEAK_HBM_GBPS,
+        "algorithmic_bytes_per_step": bp + bq,
+        "pre_us": pre_ms * 1e3,
+        "post_us": post_ms * 1e3,
+        "pre_gbps": pre_gbps,
+        "post_gbps": post_gbps,
+        "roofline": {"kernel": "post_kernel (mhc_post)", "bound": "hbm", "achieved": post_gbps,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": post_gbps / PEAK_HBM_GBPS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": bq},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="prefill-d7168")
+    ap.add_argument("--n-splits", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--summarize-rocprof", metavar="DIR")
+    args = ap.parse_args()
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: there is no multi-GPU path (every token is independent, so "
+              "data parallelism over tokens needs no communication and N GPUs would each run this step on "
+              "their own tokens). Run with --gpus 1.", file=sys.stderr)
+        raise SystemExit(2)
+    run(args)
+
+
+if __name__ == "__main__":
+    main()
