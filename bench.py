@@ -168,6 +168,7 @@ def run(args):
         })
     ws_bytes = mhc.mhc_pre_workspace_bytes(T, n, D, spec.n_splits, 0 if spec.dtype == "bf16" else 1)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    ws[:256].zero_()   # status words of a fresh workspace
     S = mhc.mhc_pre_splits(T, n, D, spec.n_splits, 0 if spec.dtype == "bf16" else 1)
     stream = torch.cuda.current_stream(dev)
 
@@ -194,6 +195,20 @@ def run(args):
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     pre_ms = sum(ev[0].elapsed_time(ev[1]) for ev in events) / args.steps
     post_ms = sum(ev[1].elapsed_time(ev[2]) for ev in events) / args.steps
+
+    # practical ceiling: a 1 GiB device-to-device copy kernel on the same stream
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (1 << 30) * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
 
     bp, bq = pre_bytes(T, n, D, e), post_bytes(T, n, D, e)
     step_gbps = (bp + bq) / (ms_per_step * 1e-3) / 1e9
@@ -222,6 +237,8 @@ def run(args):
         "post_us": post_ms * 1e3,
         "pre_gbps": pre_gbps,
         "post_gbps": post_gbps,
+        "copy_gbps_1GiB": copy_gbps,
+        "hbm_frac_of_copy": step_gbps / copy_gbps,
         "roofline": {"kernel": "post_kernel (mhc_post)", "bound": "hbm", "achieved": post_gbps,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": post_gbps / PEAK_HBM_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": bq},

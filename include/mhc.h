@@ -96,9 +96,17 @@ MHC_API size_t mhc_pre_workspace_bytes(int64_t T, int n, int64_t D, int n_splits
  * Knobs: sinkhorn_repeat >= 1; eps > 0; n_splits = split-K partials over the
  *   hidden axis (0 = library choice, else 1..256; any value gives the same
  *   result up to fp32 reassociation, and a fixed value is bitwise repeatable).
+ * Paths: bf16 with D a multiple of 128 (D <= 16384) and n_splits = D / 128
+ *   runs the single-pass kernel (the residual is read once; the workgroups
+ *   of a token tile exchange partial sums through the workspace); any other
+ *   call runs the two-pass path (pack fn, split-K GEMM, then an epilogue that
+ *   reads the residual again for y).
  * Workspace: device memory of at least mhc_pre_workspace_bytes(...) bytes,
- *   256-byte aligned, owned by the caller, not shared by concurrent calls;
- *   its contents on entry do not matter.
+ *   256-byte aligned, owned by the caller, not shared by concurrent calls.
+ *   Its first 256 bytes are status words that the single-pass path keeps
+ *   between calls: they must be zero before the first call on a workspace
+ *   (and again if anything other than mhc_pre wrote the workspace since);
+ *   the rest may hold anything.
  */
 MHC_API int mhc_pre(float* post, float* comb, void* y,
                     const void* residual, mhc_dtype dt,
@@ -106,6 +114,18 @@ MHC_API int mhc_pre(float* post, float* comb, void* y,
                     int64_t T, int n, int64_t D,
                     int sinkhorn_repeat, float eps, int n_splits,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * 1 if the last mhc_pre call on `workspace` hit an exchange time-out, else 0
+ * (synchronises `stream`, then copies 16 bytes to the host). The single-pass
+ * path exchanges partial sums between the workgroups of a token tile through
+ * the workspace; a workgroup that waits longer than 100 ms gives up (so the
+ * call always finishes) and marks the call, whose outputs are then invalid.
+ * Always 0 after a two-pass call. The sizes and knobs must be those of that
+ * call. For tests and health checks: it blocks the host.
+ */
+MHC_API int mhc_pre_sync_timeouts(const void* workspace, size_t workspace_bytes, int64_t T, int n, int64_t D,
+                                  int n_splits, mhc_dtype dt, void* stream);
 
 /*
  * mhc_post - [P1] section 2 (the post call, into a tensor shaped like the

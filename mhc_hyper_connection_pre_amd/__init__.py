@@ -18,7 +18,7 @@ import os
 
 __all__ = [
     "MhcError", "lib", "library_path", "mhc_pre", "mhc_post", "mhc_post_combine_norm",
-    "mhc_pre_workspace_bytes", "mhc_pre_splits", "MHC_BF16", "MHC_F32",
+    "mhc_pre_workspace_bytes", "mhc_pre_splits", "mhc_pre_sync_timeouts", "MHC_BF16", "MHC_F32",
 ]
 
 MHC_BF16 = 0
@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
     L.mhc_pre_splits.restype = I
     L.mhc_pre_workspace_bytes.argtypes = [I64, I, I64, I, I]
     L.mhc_pre_workspace_bytes.restype = SZ
+    L.mhc_pre_sync_timeouts.argtypes = [P, SZ, I64, I, I64, I, I, P]
+    L.mhc_pre_sync_timeouts.restype = I
     L.mhc_pre.argtypes = [P, P, P, P, I, P, P, P, I64, I, I64, I, F, I, P, SZ, P]
     L.mhc_pre.restype = I
     L.mhc_post.argtypes = [P, P, P, P, P, I, I64, I, I64, P]
@@ -120,6 +122,16 @@ def mhc_pre_workspace_bytes(T: int, n: int, D: int, n_splits: int = 0, dtype_cod
     return lib().mhc_pre_workspace_bytes(T, n, D, n_splits, dtype_code)
 
 
+def mhc_pre_sync_timeouts(workspace, residual, n_splits: int = 0, stream=None) -> int:
+    """Poll timeouts the last mhc_pre on ``workspace`` (for ``residual``'s shape) recorded. Blocks the host."""
+    T, n, D = residual.shape
+    st = lib().mhc_pre_sync_timeouts(_ptr(workspace), workspace.numel(), T, n, D, n_splits, _dtype_code(residual),
+                                     _stream(residual.device, stream))
+    if st < 0:
+        raise MhcError("mhc_pre_sync_timeouts", st)
+    return st
+
+
 def mhc_pre(residual, fn, hc_scale, bias, *, sinkhorn_repeat: int = 20, eps: float = 1e-6, n_splits: int = 0,
             post=None, comb=None, y=None, workspace=None, stream=None):
     """post [T, n] f32, comb [T, n, n] f32, y [T, D] = mhc_pre(residual [T, n, D], fn, hc_scale, bias)."""
@@ -141,7 +153,9 @@ def mhc_pre(residual, fn, hc_scale, bias, *, sinkhorn_repeat: int = 20, eps: flo
     _check(y, (T, D), residual.dtype, dev, "y")
     need = L.mhc_pre_workspace_bytes(T, n, D, n_splits, dt)
     if workspace is None:
+        # a fresh workspace: zeroing the status words makes the kernels clear the rest
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        workspace[:256].zero_()
     st = L.mhc_pre(_ptr(post), _ptr(comb), _ptr(y), _ptr(residual), dt, _ptr(fn), _ptr(hc_scale), _ptr(bias),
                    T, n, D, sinkhorn_repeat, eps, n_splits, _ptr(workspace), workspace.numel(),
                    _stream(dev, stream))

@@ -23,8 +23,6 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 int vec_elems(mhc_dtype dt) { return dt == MHC_BF16 ? 8 : 4; }
 
-size_t elem_bytes(mhc_dtype dt) { return dt == MHC_BF16 ? 2 : 4; }
-
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Shape checks shared by every entry point.
@@ -84,11 +82,28 @@ int make_pre_plan(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, PrePl
   if (S > q.ksteps) S = q.ksteps;
   q.steps_per_split = (q.ksteps + S - 1) / S;
   q.S = (q.ksteps + q.steps_per_split - 1) / q.steps_per_split;  // no empty split
-  q.off_fnp = 0;
+  q.off_fnp = kStatusBytes;
   q.fnp_bytes = dt == MHC_BF16 ? (size_t)q.ksteps * q.NCB * 64 * 16 : 0;
-  q.off_part = align_up(q.fnp_bytes, 256);
+  q.off_part = align_up(q.off_fnp + q.fnp_bytes, 256);
   q.part_bytes = (size_t)q.S * (size_t)T * q.NP * sizeof(float);
-  q.total_bytes = align_up(q.off_part + q.part_bytes, 256);
+  size_t total2 = align_up(q.off_part + q.part_bytes, 256);
+  // Single-pass path: when the shape allows it and the caller asks for exactly
+  // its split count (D / 128).
+  const int fS = fused_supported(T, n, D, dt) ? fused_splits(D) : 0;
+  q.fused = fS > 0 && n_splits == fS;
+  q.fS = fS;
+  size_t totalf = 0;
+  if (q.fused) {
+    // status, then the tagged exchange words: partials [fS][T][N + 1] and pre
+    // [T][4], 8 bytes each (fn is packed inside the kernel)
+    const int tm = fused_tile_tokens();
+    q.ftiles = (int)((T + tm - 1) / tm);
+    q.off_fpart = kStatusBytes;
+    q.off_pre = align_up(q.off_fpart + (size_t)fS * (size_t)T * (q.N + 1) * 8, 256);
+    q.off_tags_end = align_up(q.off_pre + (size_t)T * 4 * 8, 256);
+    totalf = q.off_tags_end;
+  }
+  q.total_bytes = total2 > totalf ? total2 : totalf;
   *p = q;
   return MHC_OK;
 }
@@ -116,7 +131,7 @@ MHC_API const char* mhc_last_error(void) { return g_last_error; }
 MHC_API int mhc_pre_splits(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt) {
   PrePlan p;
   const int st = make_pre_plan(T, n, D, n_splits, dt, &p);
-  return st != MHC_OK ? st : p.S;
+  return st != MHC_OK ? st : (p.fused ? p.fS : p.S);
 }
 
 MHC_API size_t mhc_pre_workspace_bytes(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt) {
@@ -139,19 +154,44 @@ MHC_API int mhc_pre(float* post, float* comb, void* y, const void* residual, mhc
     return MHC_ERR_MISALIGNED;
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.total_bytes) return MHC_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (p.fused) {
+    const int capacity = fused_resident_capacity(n);
+    if (capacity >= p.fS) {
+      e = launch_pre_fused(p, residual, fn, hc_scale, bias, post, comb, y, workspace, sinkhorn_repeat, eps,
+                           capacity, s);
+      return e == hipSuccess ? MHC_OK : hip_fail(e);
+    }
+  }
+  // Two-pass path (also the fallback when the device cannot hold a tile's
+  // single-pass workgroups at once).
   char* ws = static_cast<char*>(workspace);
   float* part = reinterpret_cast<float*>(ws + p.off_part);
   void* fnp = ws + p.off_fnp;
-  hipError_t e;
   if (dt == MHC_BF16) {
     e = launch_pack_fn(p, fn, fnp, s);
     if (e != hipSuccess) return hip_fail(e);
   }
   e = launch_pre_gemm(p, residual, fnp, fn, part, s);
   if (e != hipSuccess) return hip_fail(e);
-  e = launch_pre_epilogue(p, residual, part, hc_scale, bias, post, comb, y, sinkhorn_repeat, eps, s);
+  e = launch_pre_epilogue(p, residual, part, hc_scale, bias, post, comb, y, sinkhorn_repeat, eps,
+                          reinterpret_cast<unsigned long long*>(ws), s);
   if (e != hipSuccess) return hip_fail(e);
   return MHC_OK;
+}
+
+MHC_API int mhc_pre_sync_timeouts(const void* workspace, size_t workspace_bytes, int64_t T, int n, int64_t D,
+                                  int n_splits, mhc_dtype dt, void* stream) {
+  PrePlan p;
+  const int st = make_pre_plan(T, n, D, n_splits, dt, &p);
+  if (st != MHC_OK) return st;
+  if (!p.fused || T == 0) return 0;
+  if (!workspace || workspace_bytes < p.total_bytes) return MHC_ERR_WORKSPACE;
+  unsigned long long v[2] = {0, 0};   // kStEpoch, kStTimeout
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = hipMemcpy(v, workspace, sizeof v, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e);
+  return v[0] != 0 && v[1] == v[0] ? 1 : 0;
 }
 
 MHC_API int mhc_post(void* out, const void* h, const void* residual, const float* post, const float* comb,

@@ -73,6 +73,12 @@ template <> struct Vec<F32> {
   static __device__ __forceinline__ float round_trip(float f) { return f; }
 };
 
+// acc + lo^2 + hi^2 of a packed bf16 pair (v_dot2: products exact, fp32 sum).
+__device__ __forceinline__ float dot2_self(uint32_t w, float acc) {
+  const bf16x2 p = __builtin_bit_cast(bf16x2, w);
+  return __builtin_amdgcn_fdot2_f32_bf16(p, p, acc, false);
+}
+
 // Logistic function with IEEE division and the library expf.
 __device__ __forceinline__ float sigmoidf_ieee(float u) { return 1.0f / (1.0f + expf(-u)); }
 

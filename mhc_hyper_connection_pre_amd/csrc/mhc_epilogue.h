@@ -1,0 +1,75 @@
+// Per-token epilogue of mhc_pre on 16 lanes of a wave: RMS factor, hc_scale,
+// bias, sigmoid gates and the Sinkhorn normalisation of the comb logits.
+//
+// The pre call of sglang PR #24355 analysis ("AMD ROCm DeepSeek-V4
+// performance optimisation: Aiter MHC kernel integration"), section 2, returns
+// post and comb; the closing list of that page says the fused kernel covers
+// the Sinkhorn iterations and the normalisation. Conventions (not fixed by the
+// pages): logits are [pre | post | comb row-major]; gates are the logistic
+// function; comb = Sinkhorn(exp(Z)) with each repeat normalising rows then
+// columns; the RMS mean runs over all n*D elements with eps inside the root.
+#pragma once
+
+#include "mhc_device.h"
+
+namespace mhc {
+
+// DPP controls (within each 16-lane row of the wave).
+constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1, 0, 3, 2]: partner lane ^ 1
+constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2, 3, 0, 1]: partner lane ^ 2
+constexpr int kRowRor4 = 0x124;   // row rotate by 4
+constexpr int kRowRor8 = 0x128;   // row rotate by 8
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// One 16-lane group handles one token. Lane e of the group holds the reduced
+// column sums c = e (v0) and c = e + 16 (v1) of the token's logit row
+// (N = n(n+2) mixing sums, then the sum of squares at c = N).
+// Returns, in lane e: `gate` = sigmoid logit e for e < 2n (pre then post) and
+// `comb` = comb[e / 4][e % 4] when e / 4 < n and e % 4 < n (4 x 4 padded
+// layout). The Sinkhorn normalisations multiply by the hardware reciprocal
+// (about 1 ulp) instead of dividing. The group must be 16-lane aligned and all
+// 16 lanes must execute the call (it exchanges values within the group).
+template <int NS>
+__device__ __forceinline__ void epilogue16(float v0, float v1, const float* __restrict__ hc_scale,
+                                           const float* __restrict__ bias, float K, float eps, int repeat,
+                                           float& gate, float& comb) {
+  constexpr int N = NS * (NS + 2);
+  const int lane = threadIdx.x & 63;
+  const int gb = lane & ~15;
+  const int e = lane & 15;
+  auto col = [&](int c) {  // column sum c of this group's token
+    const float a = __shfl(v0, gb + (c & 15));
+    const float b = __shfl(v1, gb + (c & 15));
+    return c < 16 ? a : b;
+  };
+  const float ssq = col(N);
+  const float r = 1.0f / sqrtf(ssq / K + eps);
+  const int i = e >> 2, jj = e & 3;
+  const bool act = i < NS && jj < NS;
+  const int cc = act ? 2 * NS + i * NS + jj : 0;
+  const float mc = col(cc);
+  const int cg = e < 2 * NS ? e : 0;
+  const float mg = col(cg);
+  gate = sigmoidf_ieee(hc_scale[e < NS ? 0 : 1] * (r * mg) + bias[cg]);
+  const float zc = act ? hc_scale[2] * (r * mc) + bias[cc] : -INFINITY;
+  // 4 x 4 padded layout in a 16-lane DPP row: a row of comb is a quad (quad
+  // permutations), a column is lanes j, j+4, j+8, j+12 (row rotations by 8, 4).
+  float rmax = fmaxf(zc, dpp_f32<kQuadSwap1>(zc));
+  rmax = fmaxf(rmax, dpp_f32<kQuadSwap2>(rmax));
+  float M = act ? expf(zc - rmax) : 0.0f;
+  for (int it = 0; it < repeat; ++it) {
+    float rs = M + dpp_f32<kQuadSwap1>(M);
+    rs = rs + dpp_f32<kQuadSwap2>(rs);
+    M = act ? M * __builtin_amdgcn_rcpf(rs) : 0.0f;
+    float cs = M + dpp_f32<kRowRor8>(M);
+    cs = cs + dpp_f32<kRowRor4>(cs);
+    M = act ? M * __builtin_amdgcn_rcpf(cs) : 0.0f;
+  }
+  comb = M;
+}
+
+}  // namespace mhc

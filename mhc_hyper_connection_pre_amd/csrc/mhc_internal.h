@@ -5,7 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/mhc.h"
+#include "mhc.h"
 
 namespace mhc {
 
@@ -14,16 +14,32 @@ namespace mhc {
 // NCB column blocks of 16. f32: a VALU dot-product kernel, no packing.
 struct PrePlan {
   int64_t T, D, K;
-  int n, N, NP;          // NP = per-token partial stride (N sums + 1 sum of squares, padded)
+  int n, N, NP;          // NP = per-token partial stride of the two-pass path (N sums + 1, padded)
   mhc_dtype dt;
-  int ksteps;            // bf16: K / 32 rounded up; f32: K / 256 rounded up
-  int S;                 // split-K partials actually written
+  int ksteps;            // bf16: K / 32 rounded up; f32: K / 64 rounded up
+  // two-pass path
+  int S;                 // split-K partials written
   int steps_per_split;
   int MT, NW;            // bf16: 16-row token tiles per wave, waves per workgroup
   int NCB;               // bf16: 16-column blocks of [fn_hi | fn_lo]
   int tok_per_wg;
-  size_t off_fnp, fnp_bytes, off_part, part_bytes, total_bytes;
+  size_t off_fnp, fnp_bytes, off_part, part_bytes;
+  // single-pass path (bf16, D a multiple of 128): S = D / 128 slices, 128-token tiles
+  bool fused;
+  int fS, ftiles;
+  size_t off_fpart, off_pre, off_tags_end;  // tagged exchange words [off_fpart, off_tags_end)
+  size_t total_bytes;    // enough for whichever path runs
 };
+
+// Status words at offset 0 of every workspace (kStatusBytes), as uint64. The
+// single-pass path keeps its exchange state here between calls; the two-pass
+// path clears kStMarker and kStTimeout.
+constexpr size_t kStatusBytes = 256;
+constexpr int kStEpoch = 0;     // epoch of the last finished single-pass call (0: none)
+constexpr int kStTimeout = 1;   // epoch of the last single-pass call whose polls timed out
+constexpr int kStMarker = 2;    // shape marker: the tag region was zeroed for this shape
+constexpr int kStDone = 16;     // finished workgroups of the running call (own 128-byte line)
+constexpr int kStArrive = 24;   // first-use barrier arrivals of the running call (own 128-byte line)
 
 // Fills `p`; returns MHC_OK or the status mhc_pre would return for the sizes.
 int make_pre_plan(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, PrePlan* p);
@@ -34,7 +50,16 @@ hipError_t launch_pre_gemm(const PrePlan& p, const void* residual, const void* f
                            float* part, hipStream_t s);
 hipError_t launch_pre_epilogue(const PrePlan& p, const void* residual, const float* part,
                                const float* hc_scale, const float* bias, float* post, float* comb,
-                               void* y, int repeat, float eps, hipStream_t s);
+                               void* y, int repeat, float eps, unsigned long long* status, hipStream_t s);
+hipError_t launch_pre_fused(const PrePlan& p, const void* residual, const float* fn, const float* hc_scale,
+                            const float* bias, float* post, float* comb, void* y, void* workspace, int repeat,
+                            float eps, int capacity, hipStream_t s);
+bool fused_supported(int64_t T, int n, int64_t D, mhc_dtype dt);
+int fused_splits(int64_t D);
+int fused_tile_tokens();
+// Workgroups of the single-pass kernel the current device holds at once (0 if unknown).
+int fused_resident_capacity(int n);
+
 hipError_t launch_post(const void* h, const void* residual, const float* post, const float* comb,
                        void* out, mhc_dtype dt, int64_t T, int n, int64_t D, hipStream_t s);
 hipError_t launch_post_combine_norm(void* normalized, void* out, const void* h, const void* residual,

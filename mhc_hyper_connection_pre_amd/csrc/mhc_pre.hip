@@ -23,64 +23,32 @@
 // the Sinkhorn iterations amplify.
 
 #include "mhc_device.h"
+#include "mhc_epilogue.h"
+#include "mhc_pack.h"
 #include "mhc_internal.h"
 
 namespace mhc {
 
 // ------------------------------------------------------------------ packing
-// fnp[(s * NCB + cb) * 64 + lane] holds 8 bf16: B[k][col] for
-// k = 32 s + 8 (lane / 16) + e (e = 0..7) and col = 16 cb + lane % 16, where
-// B[k][col] = hi(fn[k][col]) for col < N, lo(fn[k][col - N]) for N <= col < 2N,
-// and 0 for padding columns or k >= K. The same k-order is used for the A
-// operand, so the MFMA lane layout of the k index never matters.
 __global__ __launch_bounds__(256) void pack_fn_kernel(const float* __restrict__ fn, u32x4* __restrict__ fnp,
-                                                      int64_t K, int N, int NCB, int64_t total) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= total) return;
-  const int lane = (int)(idx & 63);
-  const int64_t sc = idx >> 6;
-  const int cb = (int)(sc % NCB);
-  const int64_t s = sc / NCB;
-  const int col = cb * 16 + (lane & 15);
-  const int64_t kb = s * 32 + (lane >> 4) * 8;
-  const bool is_hi = col < N;
-  const bool is_lo = !is_hi && col < 2 * N;
-  const int c = is_hi ? col : col - N;
-  float v[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int64_t k = kb + e;
-    float f = 0.0f;
-    if ((is_hi || is_lo) && k < K) f = fn[k * N + c];
-    const float hi = (float)(__bf16)f;
-    v[e] = is_hi ? hi : (f - hi);   // f - hi is exact in fp32
-  }
-  u32x4 out;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
-  fnp[idx] = out;
+                                                      int64_t K, int N, int NCB, int ksteps) {
+  __shared__ float tile[kPackSteps * 32 * (kPackMaxN + 1)];
+  pack_fn_block(fn, fnp, K, N, NCB, ksteps, tile);
 }
 
 hipError_t launch_pack_fn(const PrePlan& p, const float* fn, void* fnp, hipStream_t s) {
-  const int64_t total = (int64_t)p.ksteps * p.NCB * 64;
-  const unsigned blocks = (unsigned)((total + 255) / 256);
-  hipLaunchKernelGGL(pack_fn_kernel, dim3(blocks), dim3(256), 0, s, fn, reinterpret_cast<u32x4*>(fnp), p.K,
-                     p.N, p.NCB, total);
+  const unsigned blocks = (unsigned)((p.ksteps + kPackSteps - 1) / kPackSteps);
+  hipLaunchKernelGGL(pack_fn_kernel, dim3(blocks), dim3(256), 0, s, fn, reinterpret_cast<u32x4*>(fnp), p.K, p.N,
+                     p.NCB, p.ksteps);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ bf16 GEMM
-// acc + lo^2 + hi^2 of a packed bf16 pair (products exact, fp32 sum).
-__device__ __forceinline__ float dot2_self(uint32_t w, float acc) {
-  const bf16x2 p = __builtin_bit_cast(bf16x2, w);
-  return __builtin_amdgcn_fdot2_f32_bf16(p, p, acc, false);
-}
-
 // Workgroup = NW waves = one tile of 16*MT tokens x one split of the k-steps.
 // Wave w takes k-steps s_begin + w, + NW, ... (the NW waves read NW adjacent
 // 64-byte segments of every row at a time). Each wave keeps MT x NCB fp32
 // accumulator tiles; the waves are summed in LDS in a fixed order.
-template <int MT, int NW, int NCB>
+template <int MT, int NW, int NCB, int PF = 3>
 __global__ __launch_bounds__(NW * 64) void pre_gemm_bf16_kernel(const uint16_t* __restrict__ x,
                                                                 const u32x4* __restrict__ fnp,
                                                                 float* __restrict__ part, int64_t T, int64_t K,
@@ -116,44 +84,60 @@ __global__ __launch_bounds__(NW * 64) void pre_gemm_bf16_kernel(const uint16_t* 
 
   const u32x4* bl = fnp + lane;
   auto load = [&](int s, u32x4* a, u32x4* b) {
+    // Loads are unconditional from an in-bounds address (row 0 / k 0 stand in
+    // for rows past T and the K tail) and masked afterwards: no branches.
     const int64_t k = (int64_t)s * 32;
     const bool kok = k + q * 8 < K;
+    const int64_t ko = kok ? k : 0;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) a[mt] = (rok[mt] && kok) ? ld16(arow[mt] + k) : u32x4{0u, 0u, 0u, 0u};
+    for (int mt = 0; mt < MT; ++mt) {
+      const u32x4 v = ld16(arow[mt] + ko);
+      a[mt] = (rok[mt] && kok) ? v : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) b[cb] = bl[((int64_t)s * NCB + cb) * 64];
   };
 
-  int s = s_begin + w;
-  u32x4 a_cur[MT], b_cur[NCB];
-  if (s < s_end) load(s, a_cur, b_cur);
-  for (; s < s_end; s += NW) {
-    u32x4 a_nxt[MT], b_nxt[NCB];
-    const bool more = s + NW < s_end;
-    if (more) load(s + NW, a_nxt, b_nxt);
+  // Prefetch ring of PF k-steps per wave: step j of this wave is
+  // s_begin + w + j * NW. Buffer p holds step j + p; after it is consumed it
+  // is refilled with step j + p + PF (clamped to the wave's last step, so
+  // every load is in bounds and the load count per iteration is fixed).
+  const int s0 = s_begin + w;
+  const int nst = s0 < s_end ? (s_end - s0 + NW - 1) / NW : 0;
+  auto compute = [&](const u32x4* a, const u32x4* b) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const bf16x8 av = __builtin_bit_cast(bf16x8, a_cur[mt]);
+      const bf16x8 av = __builtin_bit_cast(bf16x8, a[mt]);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
-        acc[mt][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, b_cur[cb]),
-                                                              acc[mt][cb], 0, 0, 0);
+        acc[mt][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, b[cb]), acc[mt][cb], 0, 0,
+                                                              0);
       // Sum of squares from the same A fragment: v_dot2 of each bf16 pair with
       // itself. The four dwords are named explicitly: indexing the vector with
       // the unrolled loop variable inside the bit_cast made this compiler read
       // the first dword four times.
-      const u32x4 aw = a_cur[mt];
+      const u32x4 aw = a[mt];
       ss[mt] = dot2_self(aw.x, ss[mt]);
       ss[mt] = dot2_self(aw.y, ss[mt]);
       ss[mt] = dot2_self(aw.z, ss[mt]);
       ss[mt] = dot2_self(aw.w, ss[mt]);
     }
-    if (more) {
+  };
+  if (nst > 0) {
+    u32x4 abuf[PF][MT], bbuf[PF][NCB];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) a_cur[mt] = a_nxt[mt];
+    for (int p = 0; p < PF; ++p) load(s0 + min(p, nst - 1) * NW, abuf[p], bbuf[p]);
+    int j = 0;
+    for (; j + PF <= nst; j += PF) {
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) b_cur[cb] = b_nxt[cb];
+      for (int p = 0; p < PF; ++p) {
+        compute(abuf[p], bbuf[p]);
+        load(s0 + min(j + p + PF, nst - 1) * NW, abuf[p], bbuf[p]);
+      }
     }
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+      if (p < nst - j) compute(abuf[p], bbuf[p]);
   }
 
   // Lanes r16, r16+16, r16+32, r16+48 hold the same token row's squares.
@@ -285,7 +269,8 @@ template <class S, int NS, int CPT>
 __global__ __launch_bounds__(kEpiThreads) void pre_epilogue_kernel(
     const typename S::elem* __restrict__ x, const float* __restrict__ part, int nsplit, int NP,
     const float* __restrict__ hc_scale, const float* __restrict__ bias, float* __restrict__ post,
-    float* __restrict__ comb, typename S::elem* __restrict__ y, int64_t T, int64_t D, int repeat, float eps) {
+    float* __restrict__ comb, typename S::elem* __restrict__ y, int64_t T, int64_t D, int repeat, float eps,
+    unsigned long long* __restrict__ status) {
   constexpr int V = S::V;
   constexpr int N = NS * (NS + 2);
   __shared__ float pre_s[NS];
@@ -294,6 +279,13 @@ __global__ __launch_bounds__(kEpiThreads) void pre_epilogue_kernel(
   const int64_t nch = D / V;
   const typename S::elem* xt = x + t * NS * D;
   typename S::elem* yt = y + t * D;
+  // The two-pass path overwrites the region where the single-pass path keeps
+  // its tagged exchange words: clear that path's shape marker (its next call
+  // zeroes the region first) and its time-out record.
+  if (t == 0 && tid == 0) {
+    status[kStMarker] = 0;
+    status[kStTimeout] = 0;
+  }
 
   u32x4 buf[CPT][NS];
 #pragma unroll
@@ -305,43 +297,32 @@ __global__ __launch_bounds__(kEpiThreads) void pre_epilogue_kernel(
   }
 
   if (tid < kWave) {
+    // Lane e of wave 0 sums columns e and e + 16 of the split partials (the
+    // sum of squares is column N) in ascending split order; the loads of each
+    // group of 8 splits are in flight together. Lanes 16..63 repeat lane & 15.
     const int e = tid & 15;
-    const int i = e >> 2, jj = e & 3;
-    const bool act = i < NS && jj < NS;
     const float* pt = part + t * NP;
     const int64_t sstride = T * NP;
-    float ssq = 0.0f;
-    for (int sp = 0; sp < nsplit; ++sp) ssq += pt[sp * sstride + N];
-    const float r = 1.0f / sqrtf(ssq / (float)(NS * D) + eps);
-
-    float zc = -INFINITY;
-    if (act) {
-      const int c = 2 * NS + i * NS + jj;
-      float m = 0.0f;
-      for (int sp = 0; sp < nsplit; ++sp) m += pt[sp * sstride + c];
-      zc = hc_scale[2] * (r * m) + bias[c];
+    float v0 = 0.0f, v1 = 0.0f;
+    for (int sp0 = 0; sp0 < nsplit; sp0 += 8) {
+      float a0[8], a1[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool in = sp0 + u < nsplit;
+        a0[u] = (in && e <= N) ? pt[(int64_t)(sp0 + u) * sstride + e] : 0.0f;
+        a1[u] = (in && e + 16 <= N) ? pt[(int64_t)(sp0 + u) * sstride + e + 16] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        v0 += a0[u];
+        v1 += a1[u];
+      }
     }
-    if (tid < 2 * NS) {
-      const int c = tid;
-      float m = 0.0f;
-      for (int sp = 0; sp < nsplit; ++sp) m += pt[sp * sstride + c];
-      const float g = sigmoidf_ieee(hc_scale[c < NS ? 0 : 1] * (r * m) + bias[c]);
-      if (c < NS) pre_s[c] = g;
-      else post[t * NS + (c - NS)] = g;
-    }
-    float rmax = zc;
-    rmax = fmaxf(rmax, __shfl_xor(rmax, 1));
-    rmax = fmaxf(rmax, __shfl_xor(rmax, 2));
-    float M = act ? expf(zc - rmax) : 0.0f;
-    for (int it = 0; it < repeat; ++it) {
-      float rs = M + __shfl_xor(M, 1);
-      rs = rs + __shfl_xor(rs, 2);
-      M = act ? M / rs : 0.0f;
-      float cs = M + __shfl_xor(M, 4);
-      cs = cs + __shfl_xor(cs, 8);
-      M = act ? M / cs : 0.0f;
-    }
-    if (act && tid < 16) comb[t * NS * NS + i * NS + jj] = M;
+    float gate, combv;
+    epilogue16<NS>(v0, v1, hc_scale, bias, (float)(NS * D), eps, repeat, gate, combv);
+    if (tid < NS) pre_s[tid] = gate;
+    else if (tid < 2 * NS) post[t * NS + (tid - NS)] = gate;
+    if (tid < 16 && (e >> 2) < NS && (e & 3) < NS) comb[t * NS * NS + (e >> 2) * NS + (e & 3)] = combv;
   }
   __syncthreads();
 
@@ -389,7 +370,7 @@ __global__ __launch_bounds__(kEpiThreads) void pre_epilogue_kernel(
 template <class S, int NS>
 static hipError_t launch_epi_n(const PrePlan& p, const void* residual, const float* part, const float* hc_scale,
                                const float* bias, float* post, float* comb, void* y, int repeat, float eps,
-                               hipStream_t s) {
+                               unsigned long long* status, hipStream_t s) {
   typedef typename S::elem E;
   const int64_t nch = p.D / S::V;
   int cpt = (int)((nch + kEpiThreads - 1) / kEpiThreads);
@@ -399,7 +380,7 @@ static hipError_t launch_epi_n(const PrePlan& p, const void* residual, const flo
   E* yy = static_cast<E*>(y);
 #define MHC_EPI(C)                                                                                                 \
   hipLaunchKernelGGL((pre_epilogue_kernel<S, NS, C>), grid, block, 0, s, x, part, p.S, p.NP, hc_scale, bias, post, \
-                     comb, yy, p.T, p.D, repeat, eps)
+                     comb, yy, p.T, p.D, repeat, eps, status)
   switch (cpt) {
     case 1: MHC_EPI(1); break;
     case 2: MHC_EPI(2); break;
@@ -413,20 +394,21 @@ static hipError_t launch_epi_n(const PrePlan& p, const void* residual, const flo
 template <class S>
 static hipError_t launch_epi_s(const PrePlan& p, const void* residual, const float* part, const float* hc_scale,
                                const float* bias, float* post, float* comb, void* y, int repeat, float eps,
-                               hipStream_t s) {
+                               unsigned long long* status, hipStream_t s) {
   switch (p.n) {
-    case 1: return launch_epi_n<S, 1>(p, residual, part, hc_scale, bias, post, comb, y, repeat, eps, s);
-    case 2: return launch_epi_n<S, 2>(p, residual, part, hc_scale, bias, post, comb, y, repeat, eps, s);
-    case 3: return launch_epi_n<S, 3>(p, residual, part, hc_scale, bias, post, comb, y, repeat, eps, s);
-    default: return launch_epi_n<S, 4>(p, residual, part, hc_scale, bias, post, comb, y, repeat, eps, s);
+    case 1: return launch_epi_n<S, 1>(p, residual, part, hc_scale, bias, post, comb, y, repeat, eps, status, s);
+    case 2: return launch_epi_n<S, 2>(p, residual, part, hc_scale, bias, post, comb, y, repeat, eps, status, s);
+    case 3: return launch_epi_n<S, 3>(p, residual, part, hc_scale, bias, post, comb, y, repeat, eps, status, s);
+    default: return launch_epi_n<S, 4>(p, residual, part, hc_scale, bias, post, comb, y, repeat, eps, status, s);
   }
 }
 
 hipError_t launch_pre_epilogue(const PrePlan& p, const void* residual, const float* part, const float* hc_scale,
                                const float* bias, float* post, float* comb, void* y, int repeat, float eps,
-                               hipStream_t s) {
-  if (p.dt == MHC_F32) return launch_epi_s<F32>(p, residual, part, hc_scale, bias, post, comb, y, repeat, eps, s);
-  return launch_epi_s<BF16>(p, residual, part, hc_scale, bias, post, comb, y, repeat, eps, s);
+                               unsigned long long* status, hipStream_t s) {
+  if (p.dt == MHC_F32)
+    return launch_epi_s<F32>(p, residual, part, hc_scale, bias, post, comb, y, repeat, eps, status, s);
+  return launch_epi_s<BF16>(p, residual, part, hc_scale, bias, post, comb, y, repeat, eps, status, s);
 }
 
 }  // namespace mhc

@@ -96,14 +96,21 @@ def test_pre_plan(L):
     assert L.mhc_pre_splits(1, 5, 8, 0, BF16) == UNSUPPORTED
     assert L.mhc_pre_workspace_bytes(0, 4, 64, 0, BF16) == 0
     assert L.mhc_pre_workspace_bytes(16, 5, 64, 0, BF16) == 0
-    # workspace: packed fn (K/32 x 3 column blocks x 1 KiB) + partials [S, T, 28] fp32, 256-aligned
+    # two-pass workspace: 256 B of status words, packed fn (K/32 k-steps x 3
+    # column blocks x 1 KiB), partials [S, T, 28] fp32
     T, n, D = 2048, 4, 7168
-    S = L.mhc_pre_splits(T, n, D, 0, BF16)
-    ws = L.mhc_pre_workspace_bytes(T, n, D, 0, BF16)
     fnp = (n * D // 32) * 3 * 1024
-    part = S * T * 28 * 4
-    assert ws == (fnp + 255) // 256 * 256 + (part + 255) // 256 * 256 or ws >= fnp + part
-    assert L.mhc_pre_workspace_bytes(8, 4, 256, 0, F32) == (L.mhc_pre_splits(8, 4, 256, 0, F32) * 8 * 28 * 4 + 255) // 256 * 256
+    ws16 = L.mhc_pre_workspace_bytes(T, n, D, 16, BF16)
+    assert L.mhc_pre_splits(T, n, D, 16, BF16) == 16
+    assert ws16 == 256 + (fnp + 255) // 256 * 256 + (16 * T * 28 * 4 + 255) // 256 * 256
+    # single-pass workspace (auto when D % 128 == 0 and D <= 16384): status,
+    # then 8-byte tagged words: partials [D/128, T, 25] and pre [T, 4]
+    S = D // 128
+    assert L.mhc_pre_splits(T, n, D, S, BF16) == S == 56
+    wsS = L.mhc_pre_workspace_bytes(T, n, D, S, BF16)
+    assert wsS == 256 + (S * T * 25 * 8 + 255) // 256 * 256 + T * 4 * 8
+    # fp32 residuals always take the two-pass path (no packed fn)
+    assert L.mhc_pre_workspace_bytes(8, 4, 256, 0, F32) == 256 + (L.mhc_pre_splits(8, 4, 256, 0, F32) * 8 * 28 * 4 + 255) // 256 * 256
 
 
 def test_post_validation(L):

@@ -36,8 +36,12 @@ def _oracle_pre(x, tokens=None):
 
 def _check_pre(x, g, n_splits, tokens=None, what=""):
     s = x.spec
+    need = mhc.mhc_pre_workspace_bytes(s.T, s.n, s.D, n_splits, 0 if s.dtype == "bf16" else 1)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    ws[:256].zero_()   # a fresh workspace: cleared status words
     post, comb, y = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], sinkhorn_repeat=s.sinkhorn_repeat,
-                                eps=s.eps, n_splits=n_splits)
+                                eps=s.eps, n_splits=n_splits, workspace=ws)
+    assert mhc.mhc_pre_sync_timeouts(ws, g["residual"], n_splits) == 0, f"{what}: exchange poll timed out"
     torch.cuda.synchronize()
     hp, hc, hy = host(post), host(comb), host(y)
     if tokens is not None:
@@ -84,6 +88,95 @@ def test_small_pre_post(T, n, D, dt, sp):
     _check_post(x, g, op, oc, what=f"T{T} n{n} D{D} {dt}")
 
 
+# single-pass path: bf16 with D a multiple of 128 (tiles of 128 tokens, slices of 128)
+FUSED = [(1, 4, 512), (31, 4, 1024), (33, 4, 1536), (67, 3, 1024), (130, 2, 512), (17, 1, 2048), (64, 4, 5120),
+         (100, 4, 7168), (5, 4, 16384)]
+
+
+@pytest.mark.parametrize("T,n,D", FUSED, ids=lambda v: str(v))
+def test_fused_pre(T, n, D):
+    assert mhc.mhc_pre_splits(T, n, D, D // 128, 0) == D // 128
+    x = W.generate(W.custom(T, n, D, "bf16", seed=T * 7 + n + D, fn_std=0.02))
+    g = _gpu_inputs(x)
+    _check_pre(x, g, D // 128, what=f"single-pass T{T} n{n} D{D}")
+
+
+def test_fused_matches_two_pass():
+    x = W.generate(W.custom(96, 4, 4096, "bf16", seed=77))
+    g = _gpu_inputs(x)
+    a = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], n_splits=4096 // 128)
+    b = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], n_splits=3)
+    torch.cuda.synchronize()
+    for u, v, k in zip(a, b, ("post", "comb", "y")):
+        u = u.float().cpu().numpy().astype(np.float64)
+        v = v.float().cpu().numpy().astype(np.float64)
+        d = np.max(np.abs(u - v) / np.maximum(np.abs(v), 1e-3 if k == "y" else 1e-6))
+        assert d <= (1e-2 if k == "y" else 1e-4), (k, d)
+
+
+def _pre_into(x, g, ws, n_splits):
+    s = x.spec
+    return mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], sinkhorn_repeat=s.sinkhorn_repeat,
+                       eps=s.eps, n_splits=n_splits, workspace=ws)
+
+
+def _compare_pre(x, outs, what):
+    torch.cuda.synchronize()
+    op, oc, oy = _oracle_pre(x)
+    assert_close(host(outs[0]), op, "gate", f"{what} post")
+    assert_close(host(outs[1]), oc, "gate", f"{what} comb")
+    assert_close(host(outs[2]), oy, "tensor", f"{what} y")
+
+
+def test_workspace_reuse_across_shapes_and_paths():
+    """One workspace serves single-pass calls of two shapes and a two-pass call in between; the
+    single-pass exchange never accepts a word left by an earlier call (new inputs every call)."""
+    shapes = [(300, 4, 7168), (77, 4, 4096), (300, 4, 7168), (300, 4, 7168), (77, 4, 4096)]
+    splits = [56, 32, 16, 56, 32]
+    need = max(mhc.mhc_pre_workspace_bytes(T, n, D, sp, 0) for (T, n, D), sp in zip(shapes, splits))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ws[:256].zero_()
+    for i, ((T, n, D), sp) in enumerate(zip(shapes, splits)):
+        x = W.generate(W.custom(T, n, D, "bf16", seed=400 + i))
+        g = _gpu_inputs(x)
+        outs = _pre_into(x, g, ws, sp)
+        assert mhc.mhc_pre_sync_timeouts(ws, g["residual"], sp) == 0
+        _compare_pre(x, outs, f"reuse call {i} T{T} D{D} splits {sp}")
+
+
+def test_fused_graph_replay():
+    """The single-pass path captured in a HIP graph: every replay takes a new epoch from the
+    workspace, so each replay (new inputs copied in between, eagerly) matches the oracle."""
+    T, n, D = 200, 4, 7168
+    xs = [W.generate(W.custom(T, n, D, "bf16", seed=500 + i)) for i in range(3)]
+    g = _gpu_inputs(xs[0])
+    sp = D // 128
+    ws = torch.empty(mhc.mhc_pre_workspace_bytes(T, n, D, sp, 0), dtype=torch.uint8, device="cuda")
+    ws[:256].zero_()
+    post = torch.empty((T, n), dtype=torch.float32, device="cuda")
+    comb = torch.empty((T, n, n), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+    args = dict(sinkhorn_repeat=xs[0].spec.sinkhorn_repeat, eps=xs[0].spec.eps, n_splits=sp, workspace=ws, post=post,
+                comb=comb, y=y)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], **args)   # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], **args)
+    for i, x in enumerate(xs * 2):
+        gi = _gpu_inputs(x)
+        for k in ("residual", "fn", "hc_scale", "bias"):
+            g[k].copy_(gi[k])
+        graph.replay()
+        torch.cuda.synchronize()
+        assert mhc.mhc_pre_sync_timeouts(ws, g["residual"], sp) == 0
+        _compare_pre(x, (post, comb, y), f"graph replay {i}")
+
+
 @pytest.mark.parametrize("T,n,D,dt", [(3, 4, 64, "bf16"), (65, 4, 5120, "bf16"), (9, 2, 1024, "f32"),
                                       (4, 1, 32768, "bf16"), (2, 4, 16384, "f32")])
 def test_small_post_combine_norm(T, n, D, dt):
@@ -123,12 +216,14 @@ def test_tiny_f32_workload():
     assert_close(host(out), want_out, "tensor", "tiny out")
 
 
-@pytest.mark.parametrize("name", ["prefill-d4096", "prefill-d7168"])
-def test_prefill_workload_full(name):
+@pytest.mark.parametrize("name,n_splits", [("prefill-d4096", None), ("prefill-d7168", None), ("prefill-d7168", 16),
+                                           ("prefill-d4096", 0)])
+def test_prefill_workload_full(name, n_splits):
     x = W.generate(W.spec(name))
     s = x.spec
     g = _gpu_inputs(x)
-    post, comb, y = _check_pre(x, g, s.n_splits, what=name)
+    sp = s.n_splits if n_splits is None else n_splits
+    post, comb, y = _check_pre(x, g, sp, what=f"{name} S{sp}")
     c = host(comb).astype(np.float64)
     assert np.all(c >= 0) and np.max(np.abs(c.sum(axis=1) - 1)) <= 1e-5
     # post on the GPU's own post/comb (the benchmark's chain) and on the oracle's
@@ -156,7 +251,7 @@ def test_decode_workload(name):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("n_splits", [4, 2, 8])
+@pytest.mark.parametrize("n_splits", [4, 2, 8, 0])
 def test_large_prefill_sampled(n_splits):
     s = W.spec("prefill-t16384-d7168", n_splits=n_splits)
     x = W.generate(s)
@@ -211,7 +306,7 @@ def test_split_invariance_and_determinism():
     x = W.generate(W.custom(300, 4, 7168, "bf16", seed=8))
     g = _gpu_inputs(x)
     res = {}
-    for sp in (1, 2, 4, 8, 0):
+    for sp in (1, 2, 4, 8, 0, 56):
         a = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], n_splits=sp)
         b = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], n_splits=sp)
         torch.cuda.synchronize()
@@ -219,7 +314,7 @@ def test_split_invariance_and_determinism():
             assert torch.equal(u.view(torch.int16) if u.dtype == torch.bfloat16 else u,
                                v.view(torch.int16) if v.dtype == torch.bfloat16 else v), f"repeat differs S={sp}"
         res[sp] = [host(t) for t in a]
-    for sp in (2, 4, 8, 0):
+    for sp in (2, 4, 8, 0, 56):
         for k in (0, 1):
             d = np.max(np.abs(res[sp][k].astype(np.float64) - res[1][k]) / np.maximum(np.abs(res[1][k]), 1e-6))
             assert d <= 1e-4, (sp, k, d)
