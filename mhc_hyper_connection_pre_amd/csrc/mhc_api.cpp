@@ -41,7 +41,7 @@ int check_shape(int64_t T, int n, int64_t D, mhc_dtype dt) {
 int make_pre_plan(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, PrePlan* p) {
   int st = check_shape(T, n, D, dt);
   if (st != MHC_OK) return st;
-  if (n_splits < 0 || n_splits > 256) return MHC_ERR_INVALID_ARG;
+  if (n_splits < kSplitsSinglePass || n_splits > 256) return MHC_ERR_INVALID_ARG;
   PrePlan q{};
   q.T = T;
   q.D = D;
@@ -71,7 +71,7 @@ int make_pre_plan(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, PrePl
   }
   const int64_t groups = T > 0 ? (T + q.tok_per_wg - 1) / q.tok_per_wg : 1;
   int S = n_splits;
-  if (S == 0) {
+  if (S <= 0) {
     // Library choice: about 512 workgroups, each split at least one k-step per wave.
     int64_t want = (512 + groups - 1) / groups;
     int64_t cap = q.ksteps / q.NW;
@@ -87,23 +87,24 @@ int make_pre_plan(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, PrePl
   q.off_part = align_up(q.off_fnp + q.fnp_bytes, 256);
   q.part_bytes = (size_t)q.S * (size_t)T * q.NP * sizeof(float);
   size_t total2 = align_up(q.off_part + q.part_bytes, 256);
-  // Single-pass path: when the shape allows it and the caller asks for exactly
-  // its split count (D / 128).
-  const int fS = fused_supported(T, n, D, dt) ? fused_splits(D) : 0;
-  q.fused = fS > 0 && n_splits == fS;
-  q.fS = fS;
-  size_t totalf = 0;
-  if (q.fused) {
-    // status, then the tagged exchange words: partials [fS][T][N + 1] and pre
-    // [T][4], 8 bytes each (fn is packed inside the kernel)
-    const int tm = fused_tile_tokens();
-    q.ftiles = (int)((T + tm - 1) / tm);
-    q.off_fpart = kStatusBytes;
-    q.off_pre = align_up(q.off_fpart + (size_t)fS * (size_t)T * (q.N + 1) * 8, 256);
+  // Single-pass path: the library's choice when the shape allows it, or on
+  // request (n_splits = -1). Layout: status, packed fn (as above), then the
+  // tagged exchange words: partials [rS][T][N + 1] and pre [T][4], 8 bytes each.
+  ResidentChoice rc{};
+  const bool res_ok = n_splits <= 0 && resident_choose(T, n, D, dt, &rc);
+  if (n_splits == kSplitsSinglePass && !res_ok) return MHC_ERR_UNSUPPORTED;
+  q.res = res_ok;
+  q.total_bytes = total2;
+  if (q.res) {
+    q.rS = rc.S;
+    q.rcps = rc.cps;
+    q.rper = rc.per;
+    q.rTB = rc.TB;
+    q.off_fpart = align_up(q.off_fnp + q.fnp_bytes, 256);
+    q.off_pre = align_up(q.off_fpart + (size_t)q.rS * (size_t)T * (q.N + 1) * 8, 256);
     q.off_tags_end = align_up(q.off_pre + (size_t)T * 4 * 8, 256);
-    totalf = q.off_tags_end;
+    q.total_bytes = q.off_tags_end;
   }
-  q.total_bytes = total2 > totalf ? total2 : totalf;
   *p = q;
   return MHC_OK;
 }
@@ -131,7 +132,7 @@ MHC_API const char* mhc_last_error(void) { return g_last_error; }
 MHC_API int mhc_pre_splits(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt) {
   PrePlan p;
   const int st = make_pre_plan(T, n, D, n_splits, dt, &p);
-  return st != MHC_OK ? st : (p.fused ? p.fS : p.S);
+  return st != MHC_OK ? st : (p.res ? p.rS : p.S);
 }
 
 MHC_API size_t mhc_pre_workspace_bytes(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt) {
@@ -155,16 +156,11 @@ MHC_API int mhc_pre(float* post, float* comb, void* y, const void* residual, mhc
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.total_bytes) return MHC_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (p.fused) {
-    const int capacity = fused_resident_capacity(n);
-    if (capacity >= p.fS) {
-      e = launch_pre_fused(p, residual, fn, hc_scale, bias, post, comb, y, workspace, sinkhorn_repeat, eps,
-                           capacity, s);
-      return e == hipSuccess ? MHC_OK : hip_fail(e);
-    }
+  if (p.res) {
+    e = launch_pre_resident(p, residual, fn, hc_scale, bias, post, comb, y, workspace, sinkhorn_repeat, eps, s);
+    return e == hipSuccess ? MHC_OK : hip_fail(e);
   }
-  // Two-pass path (also the fallback when the device cannot hold a tile's
-  // single-pass workgroups at once).
+  // Two-pass path.
   char* ws = static_cast<char*>(workspace);
   float* part = reinterpret_cast<float*>(ws + p.off_part);
   void* fnp = ws + p.off_fnp;
@@ -185,7 +181,7 @@ MHC_API int mhc_pre_sync_timeouts(const void* workspace, size_t workspace_bytes,
   PrePlan p;
   const int st = make_pre_plan(T, n, D, n_splits, dt, &p);
   if (st != MHC_OK) return st;
-  if (!p.fused || T == 0) return 0;
+  if (!p.res || T == 0) return 0;
   if (!workspace || workspace_bytes < p.total_bytes) return MHC_ERR_WORKSPACE;
   unsigned long long v[2] = {0, 0};   // kStEpoch, kStTimeout
   hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));

@@ -28,15 +28,16 @@ __device__ __forceinline__ float dpp_f32(float v) {
 // One 16-lane group handles one token. Lane e of the group holds the reduced
 // column sums c = e (v0) and c = e + 16 (v1) of the token's logit row
 // (N = n(n+2) mixing sums, then the sum of squares at c = N).
-// Returns, in lane e: `gate` = sigmoid logit e for e < 2n (pre then post) and
-// `comb` = comb[e / 4][e % 4] when e / 4 < n and e % 4 < n (4 x 4 padded
-// layout). The Sinkhorn normalisations multiply by the hardware reciprocal
+// logits16 returns, in lane e: `gate` = sigmoid logit e for e < 2n (pre then
+// post), and the comb logit zc = z[2n + 4 i + j] of the 4 x 4 padded layout
+// (i = e / 4, j = e % 4; `act` when i < n and j < n). sinkhorn16 then returns
+// comb[e / 4][e % 4]. The normalisations multiply by the hardware reciprocal
 // (about 1 ulp) instead of dividing. The group must be 16-lane aligned and all
-// 16 lanes must execute the call (it exchanges values within the group).
+// 16 lanes must execute the calls (they exchange values within the group).
 template <int NS>
-__device__ __forceinline__ void epilogue16(float v0, float v1, const float* __restrict__ hc_scale,
-                                           const float* __restrict__ bias, float K, float eps, int repeat,
-                                           float& gate, float& comb) {
+__device__ __forceinline__ void logits16(float v0, float v1, const float* __restrict__ hc_scale,
+                                         const float* __restrict__ bias, float K, float eps, float& gate, float& zc,
+                                         bool& act) {
   constexpr int N = NS * (NS + 2);
   const int lane = threadIdx.x & 63;
   const int gb = lane & ~15;
@@ -49,13 +50,16 @@ __device__ __forceinline__ void epilogue16(float v0, float v1, const float* __re
   const float ssq = col(N);
   const float r = 1.0f / sqrtf(ssq / K + eps);
   const int i = e >> 2, jj = e & 3;
-  const bool act = i < NS && jj < NS;
+  act = i < NS && jj < NS;
   const int cc = act ? 2 * NS + i * NS + jj : 0;
   const float mc = col(cc);
   const int cg = e < 2 * NS ? e : 0;
   const float mg = col(cg);
   gate = sigmoidf_ieee(hc_scale[e < NS ? 0 : 1] * (r * mg) + bias[cg]);
-  const float zc = act ? hc_scale[2] * (r * mc) + bias[cc] : -INFINITY;
+  zc = act ? hc_scale[2] * (r * mc) + bias[cc] : -INFINITY;
+}
+
+__device__ __forceinline__ float sinkhorn16(float zc, bool act, int repeat) {
   // 4 x 4 padded layout in a 16-lane DPP row: a row of comb is a quad (quad
   // permutations), a column is lanes j, j+4, j+8, j+12 (row rotations by 8, 4).
   float rmax = fmaxf(zc, dpp_f32<kQuadSwap1>(zc));
@@ -69,7 +73,17 @@ __device__ __forceinline__ void epilogue16(float v0, float v1, const float* __re
     cs = cs + dpp_f32<kRowRor4>(cs);
     M = act ? M * __builtin_amdgcn_rcpf(cs) : 0.0f;
   }
-  comb = M;
+  return M;
+}
+
+template <int NS>
+__device__ __forceinline__ void epilogue16(float v0, float v1, const float* __restrict__ hc_scale,
+                                           const float* __restrict__ bias, float K, float eps, int repeat,
+                                           float& gate, float& comb) {
+  float zc;
+  bool act;
+  logits16<NS>(v0, v1, hc_scale, bias, K, eps, gate, zc, act);
+  comb = sinkhorn16(zc, act, repeat);
 }
 
 }  // namespace mhc

@@ -24,9 +24,10 @@ struct PrePlan {
   int NCB;               // bf16: 16-column blocks of [fn_hi | fn_lo]
   int tok_per_wg;
   size_t off_fnp, fnp_bytes, off_part, part_bytes;
-  // single-pass path (bf16, D a multiple of 128): S = D / 128 slices, 128-token tiles
-  bool fused;
-  int fS, ftiles;
+  // single-pass ("resident") path, bf16: 128-token tiles x S slices of the
+  // hidden axis, 32 * cps positions per stream each; `rper` tiles per launch
+  bool res;
+  int rS, rcps, rper, rTB;
   size_t off_fpart, off_pre, off_tags_end;  // tagged exchange words [off_fpart, off_tags_end)
   size_t total_bytes;    // enough for whichever path runs
 };
@@ -35,11 +36,12 @@ struct PrePlan {
 // single-pass path keeps its exchange state here between calls; the two-pass
 // path clears kStMarker and kStTimeout.
 constexpr size_t kStatusBytes = 256;
-constexpr int kStEpoch = 0;     // epoch of the last finished single-pass call (0: none)
+constexpr int kStEpoch = 0;     // epoch of the last single-pass call (advanced by its prologue)
 constexpr int kStTimeout = 1;   // epoch of the last single-pass call whose polls timed out
 constexpr int kStMarker = 2;    // shape marker: the tag region was zeroed for this shape
-constexpr int kStDone = 16;     // finished workgroups of the running call (own 128-byte line)
-constexpr int kStArrive = 24;   // first-use barrier arrivals of the running call (own 128-byte line)
+
+// n_splits value that asks for the single-pass path.
+constexpr int kSplitsSinglePass = -1;
 
 // Fills `p`; returns MHC_OK or the status mhc_pre would return for the sizes.
 int make_pre_plan(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, PrePlan* p);
@@ -51,14 +53,16 @@ hipError_t launch_pre_gemm(const PrePlan& p, const void* residual, const void* f
 hipError_t launch_pre_epilogue(const PrePlan& p, const void* residual, const float* part,
                                const float* hc_scale, const float* bias, float* post, float* comb,
                                void* y, int repeat, float eps, unsigned long long* status, hipStream_t s);
-hipError_t launch_pre_fused(const PrePlan& p, const void* residual, const float* fn, const float* hc_scale,
-                            const float* bias, float* post, float* comb, void* y, void* workspace, int repeat,
-                            float eps, int capacity, hipStream_t s);
-bool fused_supported(int64_t T, int n, int64_t D, mhc_dtype dt);
-int fused_splits(int64_t D);
-int fused_tile_tokens();
-// Workgroups of the single-pass kernel the current device holds at once (0 if unknown).
-int fused_resident_capacity(int n);
+hipError_t launch_pre_resident(const PrePlan& p, const void* residual, const float* fn, const float* hc_scale,
+                               const float* bias, float* post, float* comb, void* y, void* workspace, int repeat,
+                               float eps, hipStream_t s);
+// Single-pass tiling for the shape on the current device (or a 256-CU MI355X
+// when no device is visible): false if the shape is not supported.
+struct ResidentChoice {
+  int cps, S, per, TB;
+};
+bool resident_choose(int64_t T, int n, int64_t D, mhc_dtype dt, ResidentChoice* c);
+constexpr int kResidentTile = 128;
 
 hipError_t launch_post(const void* h, const void* residual, const float* post, const float* comb,
                        void* out, mhc_dtype dt, int64_t T, int n, int64_t D, hipStream_t s);

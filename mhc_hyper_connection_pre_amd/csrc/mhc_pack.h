@@ -15,23 +15,38 @@
 
 namespace mhc {
 
-constexpr int kPackSteps = 4;   // k-steps (32 fn rows each) per 256-thread block
+constexpr int kPackSteps = 2;   // k-steps (32 fn rows each) per 256-thread block
 constexpr int kPackMaxN = 24;   // n <= 4
 
 // One block packs k-steps [blockIdx.x * kPackSteps, ... + kPackSteps): the
-// rows are read with consecutive threads on consecutive floats into the LDS
+// rows (contiguous in fn) are read with consecutive threads on consecutive
+// 16-byte vectors (4-byte words when fn is not 16-byte aligned) into the LDS
 // `tile` (kPackSteps * 32 * (kPackMaxN + 1) floats), then each thread builds
-// one fragment; consecutive threads write consecutive fragments.
+// fragments; consecutive threads write consecutive fragments.
 __device__ __forceinline__ void pack_fn_block(const float* __restrict__ fn, u32x4* __restrict__ fnp, int64_t K,
-                                              int N, int NCB, int ksteps, float* tile) {
+                                              int N, int NCB, int ksteps, bool vec4, float* tile) {
   const int s0 = blockIdx.x * kPackSteps;
   const int64_t k0 = (int64_t)s0 * 32;
   const int64_t left = K - k0;
   const int rows = (int)(left < kPackSteps * 32 ? left : kPackSteps * 32);
   const float* src = fn + k0 * N;
-  for (int i = threadIdx.x; i < rows * N; i += blockDim.x) {
-    const int r = i / N, c = i - r * N;
-    tile[r * (N + 1) + c] = src[i];
+  const int nval = rows * N;
+  if (vec4 && (nval & 3) == 0) {
+    const f32x4* s4 = reinterpret_cast<const f32x4*>(src);
+    for (int i = threadIdx.x; i < nval / 4; i += blockDim.x) {
+      const f32x4 v = s4[i];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = 4 * i + u;
+        const int r = e / N, c = e - r * N;
+        tile[r * (N + 1) + c] = v[u];
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < nval; i += blockDim.x) {
+      const int r = i / N, c = i - r * N;
+      tile[r * (N + 1) + c] = src[i];
+    }
   }
   __syncthreads();
   for (int f = threadIdx.x; f < kPackSteps * NCB * 64; f += blockDim.x) {

@@ -31,15 +31,16 @@ namespace mhc {
 
 // ------------------------------------------------------------------ packing
 __global__ __launch_bounds__(256) void pack_fn_kernel(const float* __restrict__ fn, u32x4* __restrict__ fnp,
-                                                      int64_t K, int N, int NCB, int ksteps) {
+                                                      int64_t K, int N, int NCB, int ksteps, bool vec4) {
   __shared__ float tile[kPackSteps * 32 * (kPackMaxN + 1)];
-  pack_fn_block(fn, fnp, K, N, NCB, ksteps, tile);
+  pack_fn_block(fn, fnp, K, N, NCB, ksteps, vec4, tile);
 }
 
 hipError_t launch_pack_fn(const PrePlan& p, const float* fn, void* fnp, hipStream_t s) {
   const unsigned blocks = (unsigned)((p.ksteps + kPackSteps - 1) / kPackSteps);
+  const bool vec4 = (reinterpret_cast<uintptr_t>(fn) & 15) == 0;
   hipLaunchKernelGGL(pack_fn_kernel, dim3(blocks), dim3(256), 0, s, fn, reinterpret_cast<u32x4*>(fnp), p.K, p.N,
-                     p.NCB, p.ksteps);
+                     p.NCB, p.ksteps, vec4);
   return hipGetLastError();
 }
 

@@ -72,7 +72,7 @@ def test_pre_validation(L):
     assert pre(L, repeat=0) == INVALID
     assert pre(L, eps=0.0) == INVALID
     assert pre(L, eps=float("nan")) == INVALID
-    assert pre(L, splits=-1) == INVALID
+    assert pre(L, splits=-2) == INVALID
     assert pre(L, splits=257) == INVALID
     for k in ("post", "comb", "y", "res", "fn", "hc", "bias"):
         assert pre(L, **{k: None}) == INVALID, k
@@ -103,12 +103,18 @@ def test_pre_plan(L):
     ws16 = L.mhc_pre_workspace_bytes(T, n, D, 16, BF16)
     assert L.mhc_pre_splits(T, n, D, 16, BF16) == 16
     assert ws16 == 256 + (fnp + 255) // 256 * 256 + (16 * T * 28 * 4 + 255) // 256 * 256
-    # single-pass workspace (auto when D % 128 == 0 and D <= 16384): status,
-    # then 8-byte tagged words: partials [D/128, T, 25] and pre [T, 4]
-    S = D // 128
-    assert L.mhc_pre_splits(T, n, D, S, BF16) == S == 56
-    wsS = L.mhc_pre_workspace_bytes(T, n, D, S, BF16)
-    assert wsS == 256 + (S * T * 25 * 8 + 255) // 256 * 256 + T * 4 * 8
+    # single-pass workspace (n_splits = -1, and the library's choice for bf16
+    # when D % 32 == 0): status, packed fn, then 8-byte tagged words: partials
+    # [S, T, 25] and pre [T, 4]
+    S = L.mhc_pre_splits(T, n, D, -1, BF16)
+    assert S > 0 and D % S == 0 and (D // S) % 32 == 0
+    assert L.mhc_pre_splits(T, n, D, 0, BF16) == S
+    wsS = L.mhc_pre_workspace_bytes(T, n, D, -1, BF16)
+    assert wsS == 256 + fnp + (S * T * 25 * 8 + 255) // 256 * 256 + T * 4 * 8
+    assert L.mhc_pre_splits(T, n, 104, -1, BF16) == UNSUPPORTED        # D % 32 != 0
+    assert L.mhc_pre_splits(T, n, 104, 0, BF16) >= 1                    # ... two-pass instead
+    assert L.mhc_pre_splits(8, 4, 256, -1, F32) == UNSUPPORTED           # fp32: two-pass only
+    assert L.mhc_pre_splits(T, n, D, -2, BF16) == INVALID
     # fp32 residuals always take the two-pass path (no packed fn)
     assert L.mhc_pre_workspace_bytes(8, 4, 256, 0, F32) == 256 + (L.mhc_pre_splits(8, 4, 256, 0, F32) * 8 * 28 * 4 + 255) // 256 * 256
 

@@ -90,21 +90,36 @@ def test_small_pre_post(T, n, D, dt, sp):
 
 # single-pass path: bf16 with D a multiple of 128 (tiles of 128 tokens, slices of 128)
 FUSED = [(1, 4, 512), (31, 4, 1024), (33, 4, 1536), (67, 3, 1024), (130, 2, 512), (17, 1, 2048), (64, 4, 5120),
-         (100, 4, 7168), (5, 4, 16384)]
+         (100, 4, 7168), (5, 4, 16384), (129, 4, 1056), (300, 3, 2240), (257, 2, 448)]
 
 
 @pytest.mark.parametrize("T,n,D", FUSED, ids=lambda v: str(v))
 def test_fused_pre(T, n, D):
-    assert mhc.mhc_pre_splits(T, n, D, D // 128, 0) == D // 128
+    S = mhc.mhc_pre_splits(T, n, D, -1, 0)
+    assert S > 0 and D % S == 0 and (D // S) % 32 == 0
+    assert mhc.mhc_pre_splits(T, n, D, 0, 0) == S   # the library's choice for bf16
     x = W.generate(W.custom(T, n, D, "bf16", seed=T * 7 + n + D, fn_std=0.02))
     g = _gpu_inputs(x)
-    _check_pre(x, g, D // 128, what=f"single-pass T{T} n{n} D{D}")
+    _check_pre(x, g, -1, what=f"single-pass T{T} n{n} D{D} S{S}")
+
+
+@pytest.mark.parametrize("n_splits", [-1, 3])
+def test_unaligned_fn(n_splits):
+    """fn at a 4-byte (not 16-byte) aligned address takes the word-wise packing loads."""
+    T, n, D = 70, 4, 1024
+    x = W.generate(W.custom(T, n, D, "bf16", seed=91))
+    g = _gpu_inputs(x)
+    buf = torch.empty(g["fn"].numel() + 1, dtype=torch.float32, device="cuda")
+    buf[1:].copy_(g["fn"].reshape(-1))
+    g["fn"] = buf[1:].view(n * D, n * (n + 2))
+    assert g["fn"].data_ptr() % 16 == 4
+    _check_pre(x, g, n_splits, what=f"unaligned fn splits {n_splits}")
 
 
 def test_fused_matches_two_pass():
     x = W.generate(W.custom(96, 4, 4096, "bf16", seed=77))
     g = _gpu_inputs(x)
-    a = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], n_splits=4096 // 128)
+    a = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], n_splits=-1)
     b = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], n_splits=3)
     torch.cuda.synchronize()
     for u, v, k in zip(a, b, ("post", "comb", "y")):
@@ -132,7 +147,7 @@ def test_workspace_reuse_across_shapes_and_paths():
     """One workspace serves single-pass calls of two shapes and a two-pass call in between; the
     single-pass exchange never accepts a word left by an earlier call (new inputs every call)."""
     shapes = [(300, 4, 7168), (77, 4, 4096), (300, 4, 7168), (300, 4, 7168), (77, 4, 4096)]
-    splits = [56, 32, 16, 56, 32]
+    splits = [-1, -1, 16, -1, -1]
     need = max(mhc.mhc_pre_workspace_bytes(T, n, D, sp, 0) for (T, n, D), sp in zip(shapes, splits))
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     ws[:256].zero_()
@@ -150,7 +165,7 @@ def test_fused_graph_replay():
     T, n, D = 200, 4, 7168
     xs = [W.generate(W.custom(T, n, D, "bf16", seed=500 + i)) for i in range(3)]
     g = _gpu_inputs(xs[0])
-    sp = D // 128
+    sp = -1
     ws = torch.empty(mhc.mhc_pre_workspace_bytes(T, n, D, sp, 0), dtype=torch.uint8, device="cuda")
     ws[:256].zero_()
     post = torch.empty((T, n), dtype=torch.float32, device="cuda")
@@ -306,7 +321,7 @@ def test_split_invariance_and_determinism():
     x = W.generate(W.custom(300, 4, 7168, "bf16", seed=8))
     g = _gpu_inputs(x)
     res = {}
-    for sp in (1, 2, 4, 8, 0, 56):
+    for sp in (1, 2, 4, 8, 0, -1):
         a = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], n_splits=sp)
         b = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], n_splits=sp)
         torch.cuda.synchronize()
@@ -314,7 +329,7 @@ def test_split_invariance_and_determinism():
             assert torch.equal(u.view(torch.int16) if u.dtype == torch.bfloat16 else u,
                                v.view(torch.int16) if v.dtype == torch.bfloat16 else v), f"repeat differs S={sp}"
         res[sp] = [host(t) for t in a]
-    for sp in (2, 4, 8, 0, 56):
+    for sp in (2, 4, 8, 0, -1):
         for k in (0, 1):
             d = np.max(np.abs(res[sp][k].astype(np.float64) - res[1][k]) / np.maximum(np.abs(res[1][k]), 1e-6))
             assert d <= 1e-4, (sp, k, d)
