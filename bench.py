@@ -170,26 +170,63 @@ def run(args):
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     ws[:256].zero_()   # status words of a fresh workspace
     S = mhc.mhc_pre_splits(T, n, D, spec.n_splits, 0 if spec.dtype == "bf16" else 1)
+    try:
+        single = spec.n_splits <= 0 and mhc.mhc_pre_splits(T, n, D, -1, 0 if spec.dtype == "bf16" else 1) == S
+    except mhc.MhcError:
+        single = False
     stream = torch.cuda.current_stream(dev)
 
-    def step(b, ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def call_pre(b, st):
         mhc.mhc_pre(b["residual"], fn, hc, bias, sinkhorn_repeat=spec.sinkhorn_repeat, eps=spec.eps,
-                    n_splits=spec.n_splits, post=b["post"], comb=b["comb"], y=b["y"], workspace=ws, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        mhc.mhc_post(b["h"], b["residual"], b["post"], b["comb"], out=b["out"], stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
+                    n_splits=spec.n_splits, post=b["post"], comb=b["comb"], y=b["y"], workspace=ws, stream=st)
+
+    def call_post(b, st):
+        mhc.mhc_post(b["h"], b["residual"], b["post"], b["comb"], out=b["out"], stream=st)
 
     for i in range(args.warmup):
-        step(sets[i % nsets])
+        call_pre(sets[i % nsets], stream)
+        call_post(sets[i % nsets], stream)
+    torch.cuda.synchronize()
+
+    if not args.graph:
+        def run_pre(k):
+            call_pre(sets[k], stream)
+
+        def run_post(k):
+            call_post(sets[k], stream)
+    else:
+        # Every call of a step captured once per buffer set: a replay launches the
+        # same kernels with no host work per kernel (the single-pass path keeps
+        # its per-call state in the workspace, so replays are independent calls).
+        graphs = []
+        for k in range(nsets):
+            gp, gq = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gp):
+                call_pre(sets[k], torch.cuda.current_stream(dev))
+            with torch.cuda.graph(gq):
+                call_post(sets[k], torch.cuda.current_stream(dev))
+            graphs.append((gp, gq))
+        for k in range(nsets):   # warm replays
+            graphs[k][0].replay()
+            graphs[k][1].replay()
+        torch.cuda.synchronize()
+
+        def run_pre(k):
+            graphs[k][0].replay()
+
+        def run_post(k):
+            graphs[k][1].replay()
+
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(sets[i % nsets], events[i])
+        ev = events[i]
+        ev[0].record(stream)
+        run_pre(i % nsets)
+        ev[1].record(stream)
+        run_post(i % nsets)
+        ev[2].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -229,7 +266,9 @@ def run(args):
         "dtype": "bf16" if spec.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": spec.name, "T": T, "n": n, "D": D, "n_splits": S,
-                   "sinkhorn_repeat": spec.sinkhorn_repeat, "buffer_sets": nsets},
+                   "path": "single-pass" if single else "two-pass",
+                   "sinkhorn_repeat": spec.sinkhorn_repeat, "buffer_sets": nsets,
+                   "launch": "hip-graph replay per call" if args.graph else "direct (C-ABI call per launch)"},
         "hbm_gbps": step_gbps,
         "hbm_frac_of_peak": step_gbps / PEAK_HBM_GBPS,
         "algorithmic_bytes_per_step": bp + bq,
@@ -256,6 +295,8 @@ def main():
     ap.add_argument("--workload", default="prefill-d7168")
     ap.add_argument("--n-splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture every call in a HIP graph and replay it (measured slower than direct launches here)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--summarize-rocprof", metavar="DIR")
     args = ap.parse_args()
