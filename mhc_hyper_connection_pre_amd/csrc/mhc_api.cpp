@@ -103,7 +103,9 @@ int make_pre_plan(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, PrePl
     q.off_fpart = align_up(q.off_fnp + q.fnp_bytes, 256);
     q.off_pre = align_up(q.off_fpart + (size_t)q.rS * (size_t)T * (q.N + 1) * 8, 256);
     q.off_tags_end = align_up(q.off_pre + (size_t)T * 4 * 8, 256);
-    q.total_bytes = q.off_tags_end;
+    // also enough for the two-pass path, which a call with an fn that is not
+    // 16-byte aligned takes instead
+    q.total_bytes = q.off_tags_end > total2 ? q.off_tags_end : total2;
   }
   *p = q;
   return MHC_OK;
@@ -156,7 +158,8 @@ MHC_API int mhc_pre(float* post, float* comb, void* y, const void* residual, mhc
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.total_bytes) return MHC_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (p.res) {
+  if (p.res && !aligned(fn, 16) && n_splits == kSplitsSinglePass) return MHC_ERR_MISALIGNED;
+  if (p.res && aligned(fn, 16)) {
     e = launch_pre_resident(p, residual, fn, hc_scale, bias, post, comb, y, workspace, sinkhorn_repeat, eps, s);
     return e == hipSuccess ? MHC_OK : hip_fail(e);
   }

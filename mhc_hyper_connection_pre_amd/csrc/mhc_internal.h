@@ -25,7 +25,8 @@ struct PrePlan {
   int tok_per_wg;
   size_t off_fnp, fnp_bytes, off_part, part_bytes;
   // single-pass ("resident") path, bf16: 128-token tiles x S slices of the
-  // hidden axis, 32 * cps positions per stream each; `rper` tiles per launch
+  // hidden axis, 32 * cps positions per stream each; `rper` tiles resident at
+  // once (one generation)
   bool res;
   int rS, rcps, rper, rTB;
   size_t off_fpart, off_pre, off_tags_end;  // tagged exchange words [off_fpart, off_tags_end)
@@ -36,9 +37,11 @@ struct PrePlan {
 // single-pass path keeps its exchange state here between calls; the two-pass
 // path clears kStMarker and kStTimeout.
 constexpr size_t kStatusBytes = 256;
-constexpr int kStEpoch = 0;     // epoch of the last single-pass call (advanced by its prologue)
+constexpr int kStEpoch = 0;     // epoch of the last finished single-pass call (0: none)
 constexpr int kStTimeout = 1;   // epoch of the last single-pass call whose polls timed out
 constexpr int kStMarker = 2;    // shape marker: the tag region was zeroed for this shape
+constexpr int kStDone = 16;     // finished workgroups of the running call (own 128-byte line)
+constexpr int kStArrive = 24;   // first-use barrier arrivals of the running call (own 128-byte line)
 
 // n_splits value that asks for the single-pass path.
 constexpr int kSplitsSinglePass = -1;

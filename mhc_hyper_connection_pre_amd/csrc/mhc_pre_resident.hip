@@ -7,47 +7,49 @@
 // with the sum of squares) needs a reduction over all n*D hidden elements of a
 // token before y = sum_i pre_i x_i can be formed. A two-pass design reads the
 // residual twice. MI355X holds 512 KB of vector registers per CU (128 MB over
-// 256 CUs), enough for a whole prefill batch of residual rows (117 MB at
-// T = 2048, n = 4, D = 7168), so here every workgroup of a launch loads its
-// slice once, the slices of a token tile exchange partial sums through memory
-// once the loads are done (the memory system is then quiet, so an exchange
-// round trip is short), and y is formed from the registers.
+// 256 CUs), so a batch of residual rows stays in registers between the GEMM
+// and the stream reduce, while the slices of a token tile exchange partial
+// sums through memory.
 //
-// Work split: workgroup (tile, s) = 8 waves x 16 tokens (a 128-token tile) x
-// all n streams x hidden positions [DS s, DS s + DS), DS = 32 CPS. Wave w keeps
-// its 16 tokens x n x DS positions as MFMA A fragments (4 n CPS VGPRs: 224 at
-// n = 4, CPS = 14). All workgroups of a launch are resident at once (the host
-// sizes launches by the occupancy), so a tile's workgroups can wait for each
-// other. Per workgroup:
-//   0. the B fragments of the slice (bf16 hi/lo pairs of fn, packed by the
-//      prologue kernel into the workspace) are copied into LDS by direct
-//      global->LDS loads, in chunks of streams when the slice's fragments
-//      exceed the LDS budget; the first chunk is issued before the residual.
+// One persistent launch per call. Work item (tile, s) = 8 waves x 16 tokens
+// (a 128-token tile) x all n streams x hidden positions [DS s, DS s + DS),
+// DS = 32 CPS. Wave w keeps its 16 tokens x n x DS positions as MFMA A
+// fragments (4 n CPS VGPRs: 112 at n = 4, CPS = 7). The grid holds P = G x S
+// workgroups, all resident at once (the host sizes G by the occupancy);
+// workgroup b always takes slice s = b % S and tiles b / S, + G, + 2G, ...
+// ("generations": two of 1024 tokens at T = 2048, n = 4, D = 7168). Per
+// workgroup:
+//   0. once: its slice of fn is loaded (fp32), packed into bf16 hi/lo MFMA B
+//      fragments and kept in LDS, overlapped with the first residual loads
+// and per generation:
 //   1. split-K GEMM on v_mfma_f32_16x16x32_bf16 + sum of squares (v_dot2),
 //      each k-step as soon as its residual registers have arrived
 //   2. partial[s][token][0..N] (N mixing sums + sum of squares) published
 //   3. workgroup s finalises tokens s, s + S, ... of the tile: it reduces
-//      their S partial rows in a fixed order, runs the gates and Sinkhorn (16
-//      lanes per token), writes post and comb and publishes pre
+//      their S partial rows in a fixed order, runs the gates, publishes pre,
+//      then runs Sinkhorn (16 lanes per token) and writes post and comb
 //   4. every wave reads pre for its 16 tokens and writes y for its slice.
+// A work item waits only for the items of its tile in the same generation,
+// and every workgroup is resident, so every generation completes.
 //
 // Exchange protocol: every exchanged value is a 64-bit word, tag (low 32 bits
 // of this call's epoch) in the high half and fp32 bits in the low half,
 // written with an agent-scope relaxed atomic store (write-through) and polled
-// with agent-scope relaxed atomic loads until every tag matches. The prologue
-// advances the epoch kept in the workspace (a graph replay runs the prologue
-// too), so a word left by an earlier call never matches; it zeroes the tag
-// region when the workspace's shape marker differs (first use, another shape,
-// or the two-pass path since). Every poll gives up after 100 ms (wall clock)
-// and records the call as timed out in the workspace, so the kernel always
-// terminates.
+// with agent-scope relaxed atomic loads until every tag matches. A call uses
+// epoch = (the workspace's last epoch) + 1; the last workgroup to finish
+// records it (a graph replay is a new call too), so a word left by an earlier
+// call never matches. When the workspace's shape marker differs (first use,
+// another shape, or the two-pass path since), the workgroups first zero the
+// tag region and meet at a grid barrier. Every poll gives up after 100 ms
+// (wall clock) and records the call as timed out in the workspace, so the
+// kernel always terminates.
 
 #include <atomic>
+#include <type_traits>
 
 #include "mhc_device.h"
 #include "mhc_epilogue.h"
 #include "mhc_internal.h"
-#include "mhc_pack.h"
 
 namespace mhc {
 
@@ -76,13 +78,21 @@ __device__ __forceinline__ void st_agent(u64* p, u64 v) {
 }
 __device__ __forceinline__ bool tag_is(u64 w, unsigned tag) { return (unsigned)(w >> 32) == tag; }
 __device__ __forceinline__ float tag_val(u64 w) { return __uint_as_float((unsigned)(w & 0xffffffffull)); }
+// Arrival counter (one atomic add per workgroup; the last arrival of a call
+// sets it back to zero). Returns the count after this arrival.
+__device__ __forceinline__ u64 count_in(u64* p) {
+  return __hip_atomic_fetch_add(p, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+}
+// Wait until this wave's outstanding vector memory operations (loads and
+// stores) have completed: vmcnt = 0, other counters unconstrained.
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 
 }  // namespace
 
 struct ResArgs {
   const uint16_t* x;
-  const u32x4* fnp;   // fn packed into B fragments
+  const float* fn;
   const float* hc_scale;
   const float* bias;
   float* post;
@@ -92,8 +102,9 @@ struct ResArgs {
   u64* prebuf;        // [T][4] tagged
   u64* status;        // status words (kSt*)
   u64 marker;
+  int64_t ntag;       // tagged words from part to the end of prebuf
   int64_t T, D;
-  int S, tile0, TB, repeat;
+  int S, G, P, TB, repeat;
   float eps, K;
 };
 
@@ -105,12 +116,14 @@ struct ResShape {
   static constexpr int DS = 32 * CPS;
   static constexpr int KSW = NS * CPS;            // k-steps of a slice
   static constexpr int PER_STREAM = CPS * NCB;    // 1 KB fragment blocks per stream
-  static constexpr int BBLK = NS * PER_STREAM;     // the slice's B fragments (<= 96 KB)
+  static constexpr int BBLK = NS * PER_STREAM;     // the slice's B fragments
   static constexpr int kRed = kWaves * 16 * CW;   // per-wave partial rows
+  static constexpr int kStage = DS * (N + 1);     // fn rows of one stream while packing
   static constexpr int kGs = 16 * 32;             // finalise group sums
-  static constexpr int kScratch = kRed > kGs ? kRed : kGs;
-  // B, reused after the GEMM as the scratch
-  static constexpr size_t lds_bytes = BBLK * 1024 > kScratch * 4 ? (size_t)BBLK * 1024 : (size_t)kScratch * 4;
+  static constexpr int kScratch = kRed > kStage ? (kRed > kGs ? kRed : kGs) : (kStage > kGs ? kStage : kGs);
+  static constexpr size_t lds_bytes = (size_t)BBLK * 1024 + (size_t)kScratch * 4;   // B, then the scratch
+  static constexpr int FQ = NS * DS * N / 4;      // fn slice in 4-float pieces
+  static constexpr int FP = (FQ + kThreads - 1) / kThreads;
   static constexpr bool fits = 4 * KSW <= kMaxAVgprs && lds_bytes <= (size_t)kLdsMax;
 };
 
@@ -118,235 +131,307 @@ template <int NS, int CPS>
 __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
   typedef ResShape<NS, CPS> F;
   constexpr int N = F::N, NCB = F::NCB, CW = F::CW, KSW = F::KSW;
-  extern __shared__ u32x4 lds[];      // B, later the scratch
-  u32x4* Bl = lds;
-  float* scratch = reinterpret_cast<float*>(lds);
+  extern __shared__ u32x4 lds[];
+  u32x4* Bl = lds;                                              // B fragments, for every generation
+  float* scratch = reinterpret_cast<float*>(lds + F::BBLK * 64);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, q = lane >> 4;
-  const int S = a.S;
-  const int tile = a.tile0 + (int)(blockIdx.x / S);
+  const int S = a.S, G = a.G;
   const int sg = (int)(blockIdx.x % S);
   const int64_t T = a.T, D = a.D;
+  const int tiles = (int)((T + kTM - 1) / kTM);
   const int64_t d0 = (int64_t)sg * F::DS;
-  const int64_t row = (int64_t)tile * kTM + w * 16 + r16;
-  const bool rok = row < T;
-  const u64 epoch = ld_agent(a.status + kStEpoch);
+  u64 epoch = ld_agent(a.status + kStEpoch) + 1;
+  if ((unsigned)epoch == 0u) ++epoch;   // tag 0 never matches a zeroed word
   const unsigned tag = (unsigned)epoch;
-  if (a.tile0 == 0 && blockIdx.x == 0 && tid == 0) st_agent(a.status + kStMarker, a.marker);
+  const bool fresh = ld_agent(a.status + kStMarker) != a.marker;
 
-  // The slice's B fragments are loaded into registers first, then the
-  // residual; both complete in order, so the LDS copy of B waits only for the
-  // B loads and every MFMA only for its own residual fragment. Stream i's
-  // fragments of the slice are contiguous in the packed fn (CPS k-steps x NCB
-  // blocks x 64 lanes) and land at Bl[i * PER_STREAM * 64 ...].
-  constexpr int PS = F::PER_STREAM * 64;                  // 16-byte pieces per stream
-  constexpr int NBP = NS * PS;
-  constexpr int BP = (NBP + kThreads - 1) / kThreads;     // pieces per thread
-  u32x4 bst[BP];
-  {
-    const u32x4* src = a.fnp + (d0 / 32) * NCB * 64;
-    const int64_t sstride = (D / 32) * NCB * 64;
+  // ---- first use of the workspace for this shape: zero the tag region, then
+  // a grid barrier (every workgroup of the launch is resident). Done before
+  // any residual load, so its waits never hold back the main path.
+  if (fresh) {
+    const int64_t nthr = (int64_t)a.P * kThreads;
+    for (int64_t v = (int64_t)blockIdx.x * kThreads + tid; v < a.ntag; v += nthr) st_agent(a.part + v, 0ull);
+    wait_vm();
+    __syncthreads();
+    if (tid == 0) {
+      count_in(a.status + kStArrive);
+      const long long t0 = wall_clock64();
+      while (ld_agent(a.status + kStArrive) < (u64)a.P) {
+        if (wall_clock64() - t0 > kPollTicks) {
+          st_agent(a.status + kStTimeout, epoch);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
+  }
+
+  int tile = (int)(blockIdx.x / S);
+  u32x4 A[KSW];
+  // Residual slice of tile t (rows past T read row 0 and are never published
+  // or stored), issued column by column (k-step c of every stream), the order
+  // in which y frees the registers and the GEMM consumes them.
+  auto load_cols = [&](int t) {
+    const int64_t rw0 = (int64_t)t * kTM + w * 16 + r16;
+    const uint16_t* xr = a.x + (rw0 < T ? rw0 : 0) * NS * D + d0 + q * 8;
 #pragma unroll
-    for (int u = 0; u < BP; ++u) {
-      const int pc = tid + u * kThreads;
-      const int i = pc / PS;
-      if (pc < NBP) bst[u] = src[i * sstride + (pc - i * PS)];
+    for (int c = 0; c < CPS; ++c)
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        A[i * CPS + c] = ld16(xr + i * D + c * 32);
+        __builtin_amdgcn_sched_barrier(0);   // issue in exactly this order (the waits depend on it)
+      }
+  };
+
+  // ---- 0. fn slice -> B fragments in LDS (once), overlapped with the first
+  // residual loads. The fn rows i*D + d0 .. + DS - 1 of every stream are
+  // contiguous; all are loaded first (4-float pieces), then stream 0 of the
+  // residual, then every stream is staged in LDS and packed: fragment
+  // ((i CPS + kk) NCB + cb) 64 + l holds B[k][col] for k = 32 kk + 8 (l / 16)
+  // + e of stream i's slice and col = 16 cb + l % 16 (hi = bf16(f) in columns
+  // < N, lo = bf16(f - hi) in columns N .. 2N - 1, zero beyond).
+  {
+    f32x4 fv[F::FP];
+#pragma unroll
+    for (int u = 0; u < F::FP; ++u) {   // fn is 16-byte aligned (checked on the host)
+      const int pq0 = tid + u * kThreads;
+      const int pq = pq0 < F::FQ ? pq0 : F::FQ - 1;   // no branch: the waits stay exact
+      const int i = pq / (F::DS * N / 4);
+      const int e = (pq - i * (F::DS * N / 4)) * 4;
+      fv[u] = *reinterpret_cast<const f32x4*>(a.fn + ((int64_t)i * D + d0) * N + e);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // fn first: the packing waits only for it
+    load_cols(tile);   // the first generation's residual (tile < tiles: G <= tiles), behind the fn slice
+    // keep every load issued before the packing (the scheduler would sink the
+    // residual loads towards their MFMAs and leave few loads in flight)
+    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < NS; ++i) {
+#pragma unroll
+      for (int u = 0; u < F::FP; ++u) {
+        const int pq = tid + u * kThreads;
+        if (pq < F::FQ && pq / (F::DS * N / 4) == i) {
+          const int e0 = (pq - i * (F::DS * N / 4)) * 4;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int r = (e0 + v) / N, c = e0 + v - r * N;
+            scratch[r * (N + 1) + c] = fv[u][v];
+          }
+        }
+      }
+      __syncthreads();
+      for (int f = tid; f < F::PER_STREAM * 64; f += kThreads) {
+        const int kk = f / (NCB * 64);
+        const int cb = (f / 64) % NCB;
+        const int l = f & 63;
+        const int col = cb * 16 + (l & 15);
+        const bool is_hi = col < N, is_lo = !is_hi && col < 2 * N;
+        const int c = is_hi ? col : col - N;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xv = (is_hi || is_lo) ? scratch[(kk * 32 + (l >> 4) * 8 + e) * (N + 1) + c] : 0.0f;
+          const float hi = (float)(__bf16)xv;
+          v[e] = is_hi ? hi : xv - hi;   // xv - hi is exact in fp32
+        }
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+        Bl[i * F::PER_STREAM * 64 + f] = o;
+      }
+      __syncthreads();
     }
   }
 
-  // The residual slice (rows past T read row 0 and are never published or
-  // stored): stream 0 is issued behind B, so HBM stays busy while B arrives;
-  // the other streams follow once B is in LDS (the compiler barrier keeps
-  // that order).
-  u32x4 A[KSW];
-  const uint16_t* xr = a.x + (rok ? row : 0) * NS * D + d0 + q * 8;
-#pragma unroll
-  for (int j = 0; j < CPS; ++j) A[j] = ld16(xr + j * 32);
-#pragma unroll
-  for (int u = 0; u < BP; ++u) {
-    const int pc = tid + u * kThreads;
-    if (pc < NBP) Bl[pc] = bst[u];
-  }
-  asm volatile("" ::: "memory");
-#pragma unroll
-  for (int j = CPS; j < KSW; ++j) A[j] = ld16(xr + (j / CPS) * D + (j % CPS) * 32);
-  __syncthreads();
+  // ---- one generation: tile `tile`; NEXT = another tile follows, whose
+  // residual is loaded into the registers that y frees
+  auto generation = [&](auto next_tag) {
+    constexpr bool NEXT = decltype(next_tag)::value;
+    // this tile's residual slice is in flight (rows past T read row 0 and are
+    // never published or stored): issued before the packing for the first
+    // generation, during the previous generation's y otherwise
+    const int64_t row = (int64_t)tile * kTM + w * 16 + r16;
+    const bool rok = row < T;
 
-  // ---- 1. split-K GEMM + sum of squares
-  f32x4 acc[NCB];
+    // ---- 1. split-K GEMM + sum of squares, each k-step as its residual arrives
+    f32x4 acc[NCB];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float ss = 0.0f;
+    for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float ss = 0.0f;
 #pragma unroll
-  for (int j = 0; j < KSW; ++j) {
-    const u32x4 aw = A[j];
-    const bf16x8 av = __builtin_bit_cast(bf16x8, aw);
+    for (int c = 0; c < CPS; ++c)   // the load order
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const int j = i * CPS + c;
+        const u32x4 aw = A[j];
+        const bf16x8 av = __builtin_bit_cast(bf16x8, aw);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              av, __builtin_bit_cast(bf16x8, Bl[(j * NCB + cb) * 64 + lane]), acc[cb], 0, 0, 0);
+        ss = dot2_self(aw.x, ss);
+        ss = dot2_self(aw.y, ss);
+        ss = dot2_self(aw.z, ss);
+        ss = dot2_self(aw.w, ss);
+      }
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+
+    // ---- 2. publish the partial rows of this wave's 16 tokens (hi + lo
+    // columns combined through this wave's part of the scratch)
+    float* rw = scratch + w * (16 * CW);
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
-      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, Bl[(j * NCB + cb) * 64 + lane]),
-                                                        acc[cb], 0, 0, 0);
-    ss = dot2_self(aw.x, ss);
-    ss = dot2_self(aw.y, ss);
-    ss = dot2_self(aw.z, ss);
-    ss = dot2_self(aw.w, ss);
-  }
-  ss += __shfl_xor(ss, 16);
-  ss += __shfl_xor(ss, 32);
-  __syncthreads();   // every wave is done reading B: the scratch overwrites it
-
-  // ---- 2. publish the partial rows of this wave's 16 tokens (hi + lo
-  // columns combined through LDS)
-  float* rw = scratch + w * (16 * CW);
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) rw[(q * 4 + i) * CW + cb * 16 + r16] = acc[cb][i];
-  if (q == 0) rw[r16 * CW + NCB * 16] = ss;
-  __syncthreads();
-  for (int idx = lane; idx < 16 * (N + 1); idx += 64) {
-    const int r = idx / (N + 1);
-    const int c = idx - r * (N + 1);
-    const int64_t tok = (int64_t)tile * kTM + w * 16 + r;
-    if (tok < T) {
-      const float* rr = rw + r * CW;
-      put_tagged(a.part + ((int64_t)sg * T + tok) * (N + 1) + c, tag, c < N ? rr[c] + rr[c + N] : rr[NCB * 16]);
+      for (int i = 0; i < 4; ++i) rw[(q * 4 + i) * CW + cb * 16 + r16] = acc[cb][i];
+    if (q == 0) rw[r16 * CW + NCB * 16] = ss;
+    __syncthreads();
+    for (int idx = lane; idx < 16 * (N + 1); idx += 64) {
+      const int r = idx / (N + 1);
+      const int c = idx - r * (N + 1);
+      const int64_t tok = (int64_t)tile * kTM + w * 16 + r;
+      if (tok < T) {
+        const float* rr = rw + r * CW;
+        put_tagged(a.part + ((int64_t)sg * T + tok) * (N + 1) + c, tag, c < N ? rr[c] + rr[c + N] : rr[NCB * 16]);
+      }
     }
-  }
-  __syncthreads();   // the scratch is reused below
+    __syncthreads();   // the scratch is reused below
+    // ---- 3. finalise tokens sg, sg + S, ... of the tile, TB at a time. Thread
+    // (c = tid % 32, group = tid / 32) sums column c of splits sub, sub + SUBS,
+    // ... (sub = group % SUBS) of token group / SUBS of the batch; the SUBS sums
+    // are added in order through LDS; 16-lane group g of wave w then runs the
+    // epilogue of token 4 w + g of the batch.
+    {
+      const int TB = a.TB, SUBS = 16 / a.TB;
+      const int nmine = sg < kTM ? (kTM - 1 - sg) / S + 1 : 0;
+      const int c = tid & 31, grp = tid >> 5;
+      const int sub = grp % SUBS, mm = grp / SUBS;
+      // byte offsets from the workspace base fit 32 bits (checked on the host)
+      const char* pbase = reinterpret_cast<const char*>(a.part);
+      const uint32_t rs8 = (uint32_t)(T * (N + 1) * 8);
+      float* gs = scratch;   // [TB][SUBS][32]
+      const long long t0 = wall_clock64();
+      for (int m0 = 0; m0 < nmine; m0 += TB) {
+        const int m = m0 + mm;
+        const int64_t tok = (int64_t)tile * kTM + sg + (int64_t)S * m;
+        const bool ok = m < nmine && tok < T && c <= N;
+        const uint32_t off0 = ok ? (uint32_t)((tok * (N + 1) + c) * 8) : 0u;
+        float accm = 0.0f;
+        for (;;) {
+          u64 vv[kLoads];
+#pragma unroll
+          for (int u = 0; u < kLoads; ++u) {
+            const int sp = sub + SUBS * u;
+            vv[u] = (ok && sp < S) ? ld_agent(reinterpret_cast<const u64*>(pbase + off0 + (uint32_t)sp * rs8))
+                                   : ((u64)tag << 32);
+          }
+          bool ready = true;
+          accm = 0.0f;
+#pragma unroll
+          for (int u = 0; u < kLoads; ++u) {
+            ready = ready && tag_is(vv[u], tag);
+            accm += tag_val(vv[u]);
+          }
+          if (__syncthreads_and(ready)) break;
+          if (wall_clock64() - t0 > kPollTicks) {
+            if (tid == 0) st_agent(a.status + kStTimeout, epoch);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        gs[(mm * SUBS + sub) * 32 + c] = accm;
+        __syncthreads();
+        if (w * 4 < TB) {   // wave-uniform: all 64 lanes run the epilogue
+          const int tt = w * 4 + q;
+          const int e = lane & 15;
+          float v0 = 0.0f, v1 = 0.0f;
+          if (tt < TB)
+            for (int g = 0; g < SUBS; ++g) {
+              v0 += gs[(tt * SUBS + g) * 32 + e];
+              v1 += gs[(tt * SUBS + g) * 32 + e + 16];
+            }
+          float gate, zc;
+          bool act;
+          logits16<NS>(v0, v1, a.hc_scale, a.bias, a.K, a.eps, gate, zc, act);
+          const int64_t tk = (int64_t)tile * kTM + sg + (int64_t)S * (m0 + tt);
+          const bool mine = tt < TB && m0 + tt < nmine && tk < T;
+          // pre first: the other workgroups of the tile wait for it, not for comb
+          if (mine && e < NS) put_tagged(a.prebuf + tk * 4 + e, tag, gate);
+          const float combv = sinkhorn16(zc, act, a.repeat);
+          if (mine) {
+            if (e >= NS && e < 2 * NS) a.post[tk * NS + (e - NS)] = gate;
+            if (act) a.comb[tk * NS * NS + (e >> 2) * NS + (e & 3)] = combv;
+          }
+        }
+        __syncthreads();
+      }
+    }
 
-  // ---- 3. finalise tokens sg, sg + S, ... of the tile, TB at a time. Thread
-  // (c = tid % 32, group = tid / 32) sums column c of splits sub, sub + SUBS,
-  // ... (sub = group % SUBS) of token group / SUBS of the batch; the SUBS sums
-  // are added in order through LDS; 16-lane group g of wave w then runs the
-  // epilogue of token 4 w + g of the batch.
-  {
-    const int TB = a.TB, SUBS = 16 / a.TB;
-    const int nmine = sg < kTM ? (kTM - 1 - sg) / S + 1 : 0;
-    const int c = tid & 31, grp = tid >> 5;
-    const int sub = grp % SUBS, mm = grp / SUBS;
-    // byte offsets from the workspace base fit 32 bits (checked on the host)
-    const char* pbase = reinterpret_cast<const char*>(a.part);
-    const uint32_t rs8 = (uint32_t)(T * (N + 1) * 8);
-    float* gs = scratch;   // [TB][SUBS][32]
-    const long long t0 = wall_clock64();
-    for (int m0 = 0; m0 < nmine; m0 += TB) {
-      const int m = m0 + mm;
-      const int64_t tok = (int64_t)tile * kTM + sg + (int64_t)S * m;
-      const bool ok = m < nmine && tok < T && c <= N;
-      const uint32_t off0 = ok ? (uint32_t)((tok * (N + 1) + c) * 8) : 0u;
-      float accm = 0.0f;
+    // ---- 4. pre of this wave's 16 tokens (polled), then y for the slice
+    float pre[NS];
+    {
+      const u64* pp = a.prebuf + (rok ? row : 0) * 4;
+      const long long t0 = wall_clock64();
       for (;;) {
-        u64 vv[kLoads];
-#pragma unroll
-        for (int u = 0; u < kLoads; ++u) {
-          const int sp = sub + SUBS * u;
-          vv[u] = (ok && sp < S) ? ld_agent(reinterpret_cast<const u64*>(pbase + off0 + (uint32_t)sp * rs8))
-                                 : ((u64)tag << 32);
-        }
         bool ready = true;
-        accm = 0.0f;
 #pragma unroll
-        for (int u = 0; u < kLoads; ++u) {
-          ready = ready && tag_is(vv[u], tag);
-          accm += tag_val(vv[u]);
+        for (int i = 0; i < NS; ++i) {
+          const u64 wv = rok ? ld_agent(pp + i) : ((u64)tag << 32);
+          ready = ready && tag_is(wv, tag);
+          pre[i] = tag_val(wv);
         }
-        if (__syncthreads_and(ready)) break;
+        if (__all(ready)) break;
         if (wall_clock64() - t0 > kPollTicks) {
-          if (tid == 0) st_agent(a.status + kStTimeout, epoch);
+          if (lane == 0) st_agent(a.status + kStTimeout, epoch);
           break;
         }
         __builtin_amdgcn_s_sleep(1);
       }
-      gs[(mm * SUBS + sub) * 32 + c] = accm;
-      __syncthreads();
-      if (w * 4 < TB) {   // wave-uniform: all 64 lanes run the epilogue
-        const int tt = w * 4 + q;
-        const int e = lane & 15;
-        float v0 = 0.0f, v1 = 0.0f;
-        if (tt < TB)
-          for (int g = 0; g < SUBS; ++g) {
-            v0 += gs[(tt * SUBS + g) * 32 + e];
-            v1 += gs[(tt * SUBS + g) * 32 + e + 16];
+    }
+    // y column by column; the registers of a column are refilled with the next
+    // tile's residual right after, so those loads overlap the rest of y
+    {
+      uint16_t* yr = a.y + row * D + d0 + q * 8;
+      const int64_t nrow = (int64_t)(tile + G) * kTM + w * 16 + r16;
+      const uint16_t* nxr = a.x + (nrow < T ? nrow : 0) * NS * D + d0 + q * 8;
+#pragma unroll
+      for (int c = 0; c < CPS; ++c) {
+        float o[8], f[8];
+        Vec<BF16>::unpack(A[c], f);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) o[v] = pre[0] * f[v];
+#pragma unroll
+        for (int i = 1; i < NS; ++i) {
+          Vec<BF16>::unpack(A[i * CPS + c], f);
+#pragma unroll
+          for (int v = 0; v < 8; ++v) o[v] = fmaf(pre[i], f[v], o[v]);
+        }
+        if (rok) st16(yr + c * 32, Vec<BF16>::pack(o));
+        if constexpr (NEXT) {
+#pragma unroll
+          for (int i = 0; i < NS; ++i) {
+            A[i * CPS + c] = ld16(nxr + i * D + c * 32);
+            __builtin_amdgcn_sched_barrier(0);
           }
-        float gate, zc;
-        bool act;
-        logits16<NS>(v0, v1, a.hc_scale, a.bias, a.K, a.eps, gate, zc, act);
-        const int64_t tk = (int64_t)tile * kTM + sg + (int64_t)S * (m0 + tt);
-        const bool mine = tt < TB && m0 + tt < nmine && tk < T;
-        // pre first: the other workgroups of the tile wait for it, not for comb
-        if (mine && e < NS) put_tagged(a.prebuf + tk * 4 + e, tag, gate);
-        const float combv = sinkhorn16(zc, act, a.repeat);
-        if (mine) {
-          if (e >= NS && e < 2 * NS) a.post[tk * NS + (e - NS)] = gate;
-          if (act) a.comb[tk * NS * NS + (e >> 2) * NS + (e & 3)] = combv;
         }
       }
-      __syncthreads();
     }
-  }
+  };
+  for (; tile + G < tiles; tile += G) generation(std::true_type{});
+  if (tile < tiles) generation(std::false_type{});
 
-  // ---- 4. pre of this wave's 16 tokens (polled), then y for the slice
-  float pre[NS];
-  {
-    const u64* pp = a.prebuf + (rok ? row : 0) * 4;
-    const long long t0 = wall_clock64();
-    for (;;) {
-      bool ready = true;
-#pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        const u64 wv = rok ? ld_agent(pp + i) : ((u64)tag << 32);
-        ready = ready && tag_is(wv, tag);
-        pre[i] = tag_val(wv);
-      }
-      if (__all(ready)) break;
-      if (wall_clock64() - t0 > kPollTicks) {
-        if (lane == 0) st_agent(a.status + kStTimeout, epoch);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
+  // ---- the last workgroup to finish records the epoch and the shape marker
+  // and re-arms the counters for the next call
+  __syncthreads();
+  if (tid == 0 && count_in(a.status + kStDone) == (u64)a.P) {
+    st_agent(a.status + kStDone, 0ull);
+    st_agent(a.status + kStArrive, 0ull);
+    st_agent(a.status + kStMarker, a.marker);
+    st_agent(a.status + kStEpoch, epoch);
   }
-  if (rok) {
-    uint16_t* yr = a.y + row * D + d0 + q * 8;
-#pragma unroll
-    for (int c = 0; c < CPS; ++c) {
-      float o[8], f[8];
-      Vec<BF16>::unpack(A[c], f);
-#pragma unroll
-      for (int v = 0; v < 8; ++v) o[v] = pre[0] * f[v];
-#pragma unroll
-      for (int i = 1; i < NS; ++i) {
-        Vec<BF16>::unpack(A[i * CPS + c], f);
-#pragma unroll
-        for (int v = 0; v < 8; ++v) o[v] = fmaf(pre[i], f[v], o[v]);
-      }
-      st16(yr + c * 32, Vec<BF16>::pack(o));
-    }
-  }
-}
-
-// Prologue: pack fn into the workspace, advance the epoch, and zero the tag
-// region when the workspace was last used with another shape (or never, or by
-// the two-pass path).
-__global__ __launch_bounds__(256) void resident_prologue_kernel(const float* __restrict__ fn,
-                                                                u32x4* __restrict__ fnp, int64_t K, int N, int NCB,
-                                                                int ksteps, bool vec4, u32x4* __restrict__ tags,
-                                                                int64_t ntag16, u64* __restrict__ status,
-                                                                u64 marker) {
-  __shared__ float tile[kPackSteps * 32 * (kPackMaxN + 1)];
-  if (status[kStMarker] != marker) {   // the main kernel writes the marker, after this kernel
-    const int64_t nthr = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < ntag16; i += nthr)
-      tags[i] = u32x4{0u, 0u, 0u, 0u};
-  }
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    u64 e = status[kStEpoch] + 1;
-    if ((unsigned)e == 0u) ++e;   // tag 0 never matches a zeroed word
-    status[kStEpoch] = e;
-  }
-  pack_fn_block(fn, fnp, K, N, NCB, ksteps, vec4, tile);
 }
 
 // ------------------------------------------------------------------ host side
@@ -489,7 +574,7 @@ hipError_t launch_pre_resident(const PrePlan& p, const void* residual, const flo
   char* ws = static_cast<char*>(workspace);
   ResArgs a;
   a.x = static_cast<const uint16_t*>(residual);
-  a.fnp = reinterpret_cast<const u32x4*>(ws + p.off_fnp);
+  a.fn = fn;
   a.hc_scale = hc_scale;
   a.bias = bias;
   a.post = post;
@@ -498,34 +583,20 @@ hipError_t launch_pre_resident(const PrePlan& p, const void* residual, const flo
   a.part = reinterpret_cast<u64*>(ws + p.off_fpart);
   a.prebuf = reinterpret_cast<u64*>(ws + p.off_pre);
   a.status = reinterpret_cast<u64*>(ws);
-  a.marker = 0x6d68632d72657331ull ^ ((u64)p.T * 0x9E3779B97F4A7C15ull) ^ ((u64)p.D << 20) ^ ((u64)p.n << 56) ^
+  a.marker = 0x6d68632d72657332ull ^ ((u64)p.T * 0x9E3779B97F4A7C15ull) ^ ((u64)p.D << 20) ^ ((u64)p.n << 56) ^
              ((u64)p.rS << 8);
+  a.ntag = (int64_t)((p.off_tags_end - p.off_fpart) / 8);
   a.T = p.T;
   a.D = p.D;
   a.S = p.rS;
+  a.G = p.rper;
+  a.P = p.rper * p.rS;
   a.TB = p.rTB;
   a.repeat = repeat;
   a.eps = eps;
   a.K = (float)p.K;
-
-  const unsigned pblocks = (unsigned)((p.ksteps + kPackSteps - 1) / kPackSteps);
-  const bool vec4 = (reinterpret_cast<uintptr_t>(fn) & 15) == 0;
-  hipLaunchKernelGGL(resident_prologue_kernel, dim3(pblocks), dim3(256), 0, s, fn,
-                     reinterpret_cast<u32x4*>(ws + p.off_fnp), p.K, p.N, p.NCB, p.ksteps, vec4,
-                     reinterpret_cast<u32x4*>(ws + p.off_fpart), (int64_t)((p.off_tags_end - p.off_fpart) / 16),
-                     a.status, a.marker);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
-  const int tiles = (int)((p.T + kTM - 1) / kTM);
-  for (int t0 = 0; t0 < tiles; t0 += p.rper) {
-    const int nt = tiles - t0 < p.rper ? tiles - t0 : p.rper;
-    a.tile0 = t0;
-    dispatch(p.n, p.rcps, Launcher{&a, (unsigned)(nt * p.rS), s});
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  dispatch(p.n, p.rcps, Launcher{&a, (unsigned)a.P, s});
+  return hipGetLastError();
 }
 
 }  // namespace mhc

@@ -103,9 +103,10 @@ def test_fused_pre(T, n, D):
     _check_pre(x, g, -1, what=f"single-pass T{T} n{n} D{D} S{S}")
 
 
-@pytest.mark.parametrize("n_splits", [-1, 3])
+@pytest.mark.parametrize("n_splits", [0, 3])
 def test_unaligned_fn(n_splits):
-    """fn at a 4-byte (not 16-byte) aligned address takes the word-wise packing loads."""
+    """fn at a 4-byte (not 16-byte) aligned address: the library's choice falls back to the
+    two-pass path (word-wise packing loads); asking for the single-pass path is an error."""
     T, n, D = 70, 4, 1024
     x = W.generate(W.custom(T, n, D, "bf16", seed=91))
     g = _gpu_inputs(x)
@@ -114,6 +115,9 @@ def test_unaligned_fn(n_splits):
     g["fn"] = buf[1:].view(n * D, n * (n + 2))
     assert g["fn"].data_ptr() % 16 == 4
     _check_pre(x, g, n_splits, what=f"unaligned fn splits {n_splits}")
+    with pytest.raises(mhc.MhcError) as e:
+        mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], n_splits=-1)
+    assert e.value.status == -3
 
 
 def test_fused_matches_two_pass():
