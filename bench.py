@@ -53,6 +53,12 @@ def post_bytes(T, n, D, e):
     return T * D * e + T * n * D * e + T * (n + n * n) * 4 + T * n * D * e
 
 
+def pcn_bytes(T, n, D, e):
+    """Fused post + combine + RMSNorm writing both outputs: h, residual, post, comb, combine_w and the norm
+    weight read once; normalized [T, D] and out [T, n, D] written once."""
+    return T * D * e + T * n * D * e + T * (n + n * n) * 4 + T * n * 4 + D * 4 + T * D * e + T * n * D * e
+
+
 # ---------------------------------------------------------------- traffic from counters
 
 def source_hash(path=POST_SOURCE):
@@ -114,7 +120,11 @@ def cpu_baseline(x, min_seconds):
         t0 = time.perf_counter()
         post, comb, y = O.mhc_pre(x.residual, x.fn, x.hc_scale, x.bias, n=s.n, D=s.D, dtype=s.dtype,
                                   sinkhorn_repeat=s.sinkhorn_repeat, eps=s.eps)
-        O.mhc_post(x.h, x.residual, post, comb, n=s.n, D=s.D, dtype=s.dtype)
+        if s.combine and s.dtype == "bf16":
+            O.mhc_post_combine_norm(x.h, x.residual, post, comb, x.combine_w, x.norm_weight, n=s.n, D=s.D,
+                                    dtype=s.dtype, norm_eps=s.norm_eps)
+        else:
+            O.mhc_post(x.h, x.residual, post, comb, n=s.n, D=s.D, dtype=s.dtype)
         t_total += time.perf_counter() - t0
         reps += 1
         if reps >= 20:
@@ -153,7 +163,12 @@ def run(args):
         return torch.from_numpy(a).to(dev)
 
     fn, hc, bias = dev_t(x.fn), dev_t(x.hc_scale), dev_t(x.bias)
-    per_set = pre_bytes(T, n, D, e) + post_bytes(T, n, D, e)
+    # decode workloads end the step with the fused post + combine + RMSNorm
+    fused_tail = spec.combine and spec.dtype == "bf16"
+    if fused_tail:
+        cw, nw = dev_t(x.combine_w), dev_t(x.norm_weight)
+    tail_bytes = pcn_bytes if fused_tail else post_bytes
+    per_set = pre_bytes(T, n, D, e) + tail_bytes(T, n, D, e)
     nsets = max(2, min(8, int(3 * 256e6 // max(per_set, 1)) + 1))
     sets = []
     for k in range(nsets):
@@ -165,6 +180,7 @@ def run(args):
             "comb": torch.empty((T, n, n), dtype=torch.float32, device=dev),
             "y": torch.empty((T, D), dtype=tdt, device=dev),
             "out": torch.empty((T, n, D), dtype=tdt, device=dev),
+            "normalized": torch.empty((T, D), dtype=tdt, device=dev),
         })
     ws_bytes = mhc.mhc_pre_workspace_bytes(T, n, D, spec.n_splits, 0 if spec.dtype == "bf16" else 1)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
@@ -181,7 +197,11 @@ def run(args):
                     n_splits=spec.n_splits, post=b["post"], comb=b["comb"], y=b["y"], workspace=ws, stream=st)
 
     def call_post(b, st):
-        mhc.mhc_post(b["h"], b["residual"], b["post"], b["comb"], out=b["out"], stream=st)
+        if fused_tail:
+            mhc.mhc_post_combine_norm(b["h"], b["residual"], b["post"], b["comb"], cw, nw, norm_eps=spec.norm_eps,
+                                      normalized=b["normalized"], out=b["out"], stream=st)
+        else:
+            mhc.mhc_post(b["h"], b["residual"], b["post"], b["comb"], out=b["out"], stream=st)
 
     for i in range(args.warmup):
         call_pre(sets[i % nsets], stream)
@@ -247,7 +267,7 @@ def run(args):
     copy_gbps = 2 * (1 << 30) * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
-    bp, bq = pre_bytes(T, n, D, e), post_bytes(T, n, D, e)
+    bp, bq = pre_bytes(T, n, D, e), tail_bytes(T, n, D, e)
     step_gbps = (bp + bq) / (ms_per_step * 1e-3) / 1e9
     post_gbps = bq / (post_ms * 1e-3) / 1e9
     pre_gbps = bp / (pre_ms * 1e-3) / 1e9
@@ -278,7 +298,9 @@ def run(args):
         "post_gbps": post_gbps,
         "copy_gbps_1GiB": copy_gbps,
         "hbm_frac_of_copy": step_gbps / copy_gbps,
-        "roofline": {"kernel": "post_kernel (mhc_post)", "bound": "hbm", "achieved": post_gbps,
+        "tail": "mhc_post_combine_norm (fused, writes out too)" if fused_tail else "mhc_post",
+        "roofline": {"kernel": "post_combine_norm_kernel" if fused_tail else "post_kernel (mhc_post)",
+                     "bound": "hbm", "achieved": post_gbps,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": post_gbps / PEAK_HBM_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": bq},
     }
