@@ -131,6 +131,7 @@ template <int NS, int CPS>
 __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
   typedef ResShape<NS, CPS> F;
   constexpr int N = F::N, NCB = F::NCB, CW = F::CW, KSW = F::KSW;
+  constexpr int kFirstCols = CPS / 2;   // residual columns issued before the packing
   extern __shared__ u32x4 lds[];
   u32x4* Bl = lds;                                              // B fragments, for every generation
   float* scratch = reinterpret_cast<float*>(lds + F::BBLK * 64);
@@ -175,11 +176,12 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
   // Residual slice of tile t (rows past T read row 0 and are never published
   // or stored), issued column by column (k-step c of every stream), the order
   // in which y frees the registers and the GEMM consumes them.
-  auto load_cols = [&](int t) {
+  auto load_cols = [&](int t, auto c0_tag, auto c1_tag) {
+    constexpr int C0 = decltype(c0_tag)::value, C1 = decltype(c1_tag)::value;
     const int64_t rw0 = (int64_t)t * kTM + w * 16 + r16;
     const uint16_t* xr = a.x + (rw0 < T ? rw0 : 0) * NS * D + d0 + q * 8;
 #pragma unroll
-    for (int c = 0; c < CPS; ++c)
+    for (int c = C0; c < C1; ++c)
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         A[i * CPS + c] = ld16(xr + i * D + c * 32);
@@ -204,6 +206,11 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
       fv[u] = *reinterpret_cast<const f32x4*>(a.fn + ((int64_t)i * D + d0) * N + e);
     }
     __builtin_amdgcn_sched_barrier(0);
+    // the first half of the first generation's residual columns goes out
+    // right behind the fn slice (HBM stays busy while B is packed), the rest
+    // once B is in LDS (with all of it queued at once, the whole chip's
+    // residual requests delay the fn slice by more than the packing takes)
+    load_cols(tile, std::integral_constant<int, 0>{}, std::integral_constant<int, kFirstCols>{});
     // keep every load issued before the packing (the scheduler would sink the
     // residual loads towards their MFMAs and leave few loads in flight)
     __builtin_amdgcn_sched_barrier(0);
@@ -244,11 +251,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
     }
   }
 
-  // The first generation's residual (tile < tiles: G <= tiles) is issued once
-  // B is in LDS: with the whole chip's residual requests queued behind it, the
-  // fn slice took longer to arrive than the packing saves (57.1 against 58.5
-  // us per call at T = 2048, n = 4, D = 7168).
-  load_cols(tile);
+  load_cols(tile, std::integral_constant<int, kFirstCols>{}, std::integral_constant<int, CPS>{});
 
   // ---- one generation: tile `tile`; NEXT = another tile follows, whose
   // residual is loaded into the registers that y frees
@@ -310,7 +313,10 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
     // epilogue of token 4 w + g of the batch.
     {
       const int TB = a.TB, SUBS = 16 / a.TB;
-      const int nmine = sg < kTM ? (kTM - 1 - sg) / S + 1 : 0;
+      // tokens of the tile this workgroup finalises: sg, sg + S, ... below T
+      const int64_t left = T - (int64_t)tile * kTM;
+      const int rows = left < kTM ? (int)left : kTM;
+      const int nmine = sg < rows ? (rows - 1 - sg) / S + 1 : 0;
       const int c = tid & 31, grp = tid >> 5;
       const int sub = grp % SUBS, mm = grp / SUBS;
       // byte offsets from the workspace base fit 32 bits (checked on the host)
