@@ -8,6 +8,7 @@
 #include <cstdio>
 
 #include "mhc_internal.h"
+#include "mhc_pack.h"
 
 namespace mhc {
 namespace {
@@ -54,7 +55,7 @@ int make_pre_plan(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, PrePl
   const int kstep = dt == MHC_BF16 ? 32 : 64;
   q.ksteps = (int)((q.K + kstep - 1) / kstep);
   if (dt == MHC_BF16) {
-    q.NCB = (2 * q.N + 15) / 16;
+    q.NCB = pack_blocks(n);
     if (n_splits == 1) {  // one split: a tall workgroup of 16 waves per 16 tokens keeps the k-loop parallel
       q.MT = 1;
       q.NW = 16;

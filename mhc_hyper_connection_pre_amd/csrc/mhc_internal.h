@@ -10,8 +10,8 @@
 namespace mhc {
 
 // Tiling of the pre GEMM (residual [T, K] x fn [K, N], K = n*D, N = n(n+2)).
-// bf16: MFMA 16x16x32 tiles; B = [fn_hi | fn_lo] packed into fragment order,
-// NCB column blocks of 16. f32: a VALU dot-product kernel, no packing.
+// bf16: MFMA 16x16x32 tiles; B = [fn_hi | fn_lo | fn_lo2 of the pre columns]
+// packed into fragment order, NCB column blocks of 16. f32: a VALU dot-product kernel, no packing.
 struct PrePlan {
   int64_t T, D, K;
   int n, N, NP;          // NP = per-token partial stride of the two-pass path (N sums + 1, padded)
@@ -21,7 +21,7 @@ struct PrePlan {
   int S;                 // split-K partials written
   int steps_per_split;
   int MT, NW;            // bf16: 16-row token tiles per wave, waves per workgroup
-  int NCB;               // bf16: 16-column blocks of [fn_hi | fn_lo]
+  int NCB;               // bf16: 16-column blocks of [fn_hi | fn_lo | fn_lo2]
   int tok_per_wg;
   size_t off_fnp, fnp_bytes, off_part, part_bytes;
   // single-pass ("resident") path, bf16: 128-token tiles x S slices of the

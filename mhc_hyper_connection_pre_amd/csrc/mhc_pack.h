@@ -1,14 +1,19 @@
-// Packing of fn [K, N] fp32 into bf16 hi/lo MFMA B fragments.
+// Packing of fn [K, N] fp32 into bf16 MFMA B fragments.
 //
 // Fragment (s * NCB + cb) * 64 + lane holds 8 bf16: B[k][col] for
-// k = 32 s + 8 (lane / 16) + e (e = 0..7) and col = 16 cb + lane % 16, where
-// B[k][col] = hi(fn[k][col]) for col < N, lo(fn[k][col - N]) for
-// N <= col < 2N, and 0 for padding columns or k >= K, with hi = bf16(f) and
-// lo = bf16(f - hi). The residual is exact in bf16, so x*hi + x*lo reproduces
-// x*fn to about 2^-17 relative with fp32 MFMA accumulation (a bf16-only fn
-// perturbs the comb logits by ~1e-2, which the Sinkhorn iterations amplify).
-// The A operand uses the same k order, so the MFMA lane layout of the k index
-// never matters.
+// k = 32 s + 8 (lane / 16) + e (e = 0..7) and col = 16 cb + lane % 16, with
+// the column blocks [hi | lo | lo2 | 0]:
+//   col <  N            hi(fn[k][col])            hi  = bf16(f)
+//   N  <= col < 2N      lo(fn[k][col - N])        lo  = bf16(f - hi)
+//   2N <= col < 2N + n  lo2(fn[k][col - 2N])      lo2 = bf16(f - hi - lo)
+// and 0 beyond or for k >= K (NCB = ceil((2N + n) / 16)). Both differences
+// are exact in fp32. The residual is exact in bf16, so with fp32 MFMA
+// accumulation x*hi + x*lo reproduces x*fn to about 2^-17 relative (a bf16
+// fn alone would move the comb logits by ~1e-2, which Sinkhorn amplifies),
+// and the pre-gate columns (the first n) add x*lo2 to reach fp32 accuracy:
+// y = sum_i pre_i x_i cancels to near zero for some positions, where an error
+// of 2^-17 in pre shows against the output's own magnitude. The A operand
+// uses the same k order, so the MFMA lane layout of the k index never matters.
 #pragma once
 
 #include "mhc_device.h"
@@ -17,6 +22,31 @@ namespace mhc {
 
 constexpr int kPackSteps = 2;   // k-steps (32 fn rows each) per 256-thread block
 constexpr int kPackMaxN = 24;   // n <= 4
+
+// 16-column blocks of [hi | lo | lo2 of the pre columns] for n streams.
+__host__ __device__ constexpr int pack_blocks(int n) { return (2 * n * (n + 2) + n + 15) / 16; }
+
+// n from N = n (n + 2).
+__host__ __device__ constexpr int n_pre(int N) { return N == 3 ? 1 : (N == 8 ? 2 : (N == 15 ? 3 : 4)); }
+
+// Part `part` (0 = hi, 1 = lo, 2 = lo2) of the three-term bf16 split of x,
+// as a float (exactly representable in bf16); part 3 is a zero column.
+__device__ __forceinline__ float split3(float x, int part) {
+  const float hi = (float)(__bf16)x;
+  const float r1 = x - hi;                  // exact
+  const float lo = (float)(__bf16)r1;
+  const float r2 = r1 - lo;                 // exact
+  return part == 0 ? hi : (part == 1 ? (float)(__bf16)r1 : (part == 2 ? (float)(__bf16)r2 : 0.0f));
+}
+
+// hi, lo and lo2 words (two bf16 each) of the three-term split of the pair
+// (x0, x1); the same values as split3 parts 0, 1 and 2.
+__device__ __forceinline__ void split3_pair(float x0, float x1, uint32_t& h, uint32_t& l, uint32_t& l2) {
+  h = pack_bf16x2(x0, x1);
+  const float r0 = x0 - bf16_lo(h), r1 = x1 - bf16_hi(h);   // exact
+  l = pack_bf16x2(r0, r1);
+  l2 = pack_bf16x2(r0 - bf16_lo(l), r1 - bf16_hi(l));       // exact differences
+}
 
 // One block packs k-steps [blockIdx.x * kPackSteps, ... + kPackSteps): the
 // rows (contiguous in fn) are read with consecutive threads on consecutive
@@ -55,16 +85,14 @@ __device__ __forceinline__ void pack_fn_block(const float* __restrict__ fn, u32x
     const int lane = f & 63;
     if (s0 + sl >= ksteps) continue;
     const int col = cb * 16 + (lane & 15);
-    const bool is_hi = col < N;
-    const bool is_lo = !is_hi && col < 2 * N;
-    const int c = is_hi ? col : col - N;
+    const int part = col < N ? 0 : (col < 2 * N ? 1 : (col < 2 * N + n_pre(N) ? 2 : 3));
+    const int c = col - part * N;
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int r = sl * 32 + (lane >> 4) * 8 + e;
-      const float x = ((is_hi || is_lo) && r < rows) ? tile[r * (N + 1) + c] : 0.0f;
-      const float hi = (float)(__bf16)x;
-      v[e] = is_hi ? hi : (x - hi);  // x - hi is exact in fp32
+      const float x = (part < 3 && r < rows) ? tile[r * (N + 1) + c] : 0.0f;
+      v[e] = split3(x, part);
     }
     u32x4 out;
 #pragma unroll

@@ -7,8 +7,8 @@
 // GEMM fused with the per-token sum of squares, tiled over the hidden axis).
 //
 // Three launches on the caller's stream:
-//   1. pack_fn        fn fp32 [K, N] -> bf16 hi/lo pairs in MFMA B-fragment order
-//   2. pre_gemm       residual x [T, K] (bf16) x [fn_hi | fn_lo] on MFMA
+//   1. pack_fn        fn fp32 [K, N] -> bf16 hi/lo(/lo2) terms in MFMA B-fragment order
+//   2. pre_gemm       residual x [T, K] (bf16) x [fn_hi | fn_lo | fn_lo2] on MFMA
 //                     16x16x32, plus sum of squares with v_dot2; one fp32
 //                     partial row (N sums + sum of squares) per token and split
 //   3. pre_epilogue   one workgroup per token: fixed-order split reduction,
@@ -17,10 +17,10 @@
 //                     token row prefetched before the epilogue runs.
 // The fp32-residual path replaces 1-2 with a VALU dot-product kernel.
 //
-// fn is split as hi = bf16(fn), lo = bf16(fn - hi): x is exact in bf16, so
-// x*hi + x*lo reproduces x*fn to about 2^-17 relative, with fp32 MFMA
-// accumulation. A bf16-only fn would perturb the comb logits by ~1e-2, which
-// the Sinkhorn iterations amplify.
+// fn is split into bf16 terms hi = bf16(fn), lo = bf16(fn - hi) and, for the
+// pre-gate columns, lo2 = bf16(fn - hi - lo) (mhc_pack.h): x is exact in bf16,
+// so with fp32 MFMA accumulation the mixing sums reach about 2^-17 relative
+// (2^-24 for the pre columns).
 
 #include "mhc_device.h"
 #include "mhc_epilogue.h"
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(NW * 64) void pre_gemm_bf16_kernel(const uint16_t* 
                                                                 const u32x4* __restrict__ fnp,
                                                                 float* __restrict__ part, int64_t T, int64_t K,
                                                                 int N, int NP, int ksteps, int steps_per_split) {
-  constexpr int CW = NCB * 16 + 1;  // LDS row: padded [hi | lo] columns, then the sum of squares
+  constexpr int CW = NCB * 16 + 1;  // LDS row: padded [hi | lo | lo2] columns, then the sum of squares
   __shared__ float red[NW * MT * 16 * CW];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -159,7 +159,8 @@ __global__ __launch_bounds__(NW * 64) void pre_gemm_bf16_kernel(const uint16_t* 
   }
   __syncthreads();
 
-  // partial[split][token][c] = sum over waves of (hi + lo) for c < N, squares at c = N.
+  // partial[split][token][c] = sum over waves of (hi + lo (+ lo2 for the
+  // first n columns)) for c < N, squares at c = N.
   const int outs = MT * 16 * (N + 1);
   for (int idx = threadIdx.x; idx < outs; idx += NW * 64) {
     const int row = idx / (N + 1);
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(NW * 64) void pre_gemm_bf16_kernel(const uint16_t* 
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) {
         const float* r = red + ww * (MT * 16 * CW) + row * CW;
-        v += r[c] + r[c + N];
+        v += c < n_pre(N) ? r[c] + r[c + N] + r[c + 2 * N] : r[c] + r[c + N];
       }
     } else {
 #pragma unroll
@@ -236,8 +237,12 @@ static hipError_t launch_gemm_bf16_ncb(const PrePlan& p, const uint16_t* x, cons
       hipLaunchKernelGGL((pre_gemm_bf16_kernel<MT, NW, 2>), grid, block, 0, s, x, fnp, part, p.T, p.K, p.N, p.NP,
                          p.ksteps, p.steps_per_split);
       break;
-    default:
+    case 3:
       hipLaunchKernelGGL((pre_gemm_bf16_kernel<MT, NW, 3>), grid, block, 0, s, x, fnp, part, p.T, p.K, p.N, p.NP,
+                         p.ksteps, p.steps_per_split);
+      break;
+    default:
+      hipLaunchKernelGGL((pre_gemm_bf16_kernel<MT, NW, 4>), grid, block, 0, s, x, fnp, part, p.T, p.K, p.N, p.NP,
                          p.ksteps, p.steps_per_split);
       break;
   }

@@ -19,8 +19,9 @@
 // workgroup b always takes slice s = b % S and tiles b / S, + G, + 2G, ...
 // ("generations": two of 1024 tokens at T = 2048, n = 4, D = 7168). Per
 // workgroup:
-//   0. once: its slice of fn is loaded (fp32), packed into bf16 hi/lo MFMA B
-//      fragments and kept in LDS; the first residual loads follow it
+//   0. once: its slice of fn is loaded (fp32), split into bf16 terms (hi, lo,
+//      and lo2 for the pre columns), packed into MFMA B fragments and kept in
+//      LDS; the first residual loads follow it
 // and per generation:
 //   1. split-K GEMM on v_mfma_f32_16x16x32_bf16 + sum of squares (v_dot2),
 //      each k-step as soon as its residual registers have arrived
@@ -50,6 +51,7 @@
 #include "mhc_device.h"
 #include "mhc_epilogue.h"
 #include "mhc_internal.h"
+#include "mhc_pack.h"
 
 namespace mhc {
 
@@ -111,19 +113,24 @@ struct ResArgs {
 template <int NS, int CPS>
 struct ResShape {
   static constexpr int N = NS * (NS + 2);
-  static constexpr int NCB = (2 * N + 15) / 16;   // 16-column blocks of [fn_hi | fn_lo]
+  static constexpr int NCB = pack_blocks(NS);     // 16-column blocks of [hi | lo | lo2]
   static constexpr int CW = NCB * 16 + 1;         // partial-row scratch: columns + sum of squares
   static constexpr int DS = 32 * CPS;
   static constexpr int KSW = NS * CPS;            // k-steps of a slice
   static constexpr int PER_STREAM = CPS * NCB;    // 1 KB fragment blocks per stream
   static constexpr int BBLK = NS * PER_STREAM;     // the slice's B fragments
   static constexpr int kRed = kWaves * 16 * CW;   // per-wave partial rows
-  static constexpr int kStage = DS * (N + 1);     // fn rows of one stream while packing
   static constexpr int kGs = 16 * 32;             // finalise group sums
-  static constexpr int kScratch = kRed > kStage ? (kRed > kGs ? kRed : kGs) : (kStage > kGs ? kStage : kGs);
+  static constexpr int kScratch = kRed > kGs ? kRed : kGs;
   static constexpr size_t lds_bytes = (size_t)BBLK * 1024 + (size_t)kScratch * 4;   // B, then the scratch
-  static constexpr int FQ = NS * DS * N / 4;      // fn slice in 4-float pieces
-  static constexpr int FP = (FQ + kThreads - 1) / kThreads;
+  // packing units: (k-step, 8-row k group, VW adjacent fn columns); VW = 4
+  // (one 16-byte load per row) when the fn rows keep 16-byte alignment
+  static constexpr int VW = N % 4 == 0 ? 4 : 1;
+  static constexpr int NG = N / VW;
+  static constexpr int PU = KSW * 4 * NG;
+  static constexpr int FU = (PU + kThreads - 1) / kThreads;
+  static constexpr int NPAD = NCB * 16 - (2 * N + NS);   // zero columns past lo2
+  static constexpr int PZ = KSW * 4 * NPAD;
   static constexpr bool fits = 4 * KSW <= kMaxAVgprs && lds_bytes <= (size_t)kLdsMax;
 };
 
@@ -189,21 +196,25 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
       }
   };
 
-  // ---- 0. fn slice -> B fragments in LDS (once). The fn rows i*D + d0 .. +
-  // DS - 1 of every stream are contiguous; all are loaded (4-float pieces),
-  // then every stream is staged in LDS and packed: fragment
+  // ---- 0. fn slice -> B fragments in LDS (once). Fragment
   // ((i CPS + kk) NCB + cb) 64 + l holds B[k][col] for k = 32 kk + 8 (l / 16)
-  // + e of stream i's slice and col = 16 cb + l % 16 (hi = bf16(f) in columns
-  // < N, lo = bf16(f - hi) in columns N .. 2N - 1, zero beyond).
+  // + e of stream i's slice (fn row i D + d0 + k) and col = 16 cb + l % 16:
+  // hi = bf16(f) in columns < N, lo = bf16(f - hi) in N .. 2N - 1, lo2 =
+  // bf16(f - hi - lo) of the n pre columns next, zero beyond (mhc_pack.h).
+  // Each packing unit loads its 8 fn rows x VW columns straight into
+  // registers and writes the VW columns' hi, lo (and lo2) fragments.
   {
-    f32x4 fv[F::FP];
+    typedef typename std::conditional<F::VW == 4, f32x4, float>::type FV;
+    FV fv[F::FU][8];
 #pragma unroll
-    for (int u = 0; u < F::FP; ++u) {   // fn is 16-byte aligned (checked on the host)
-      const int pq0 = tid + u * kThreads;
-      const int pq = pq0 < F::FQ ? pq0 : F::FQ - 1;   // no branch: the waits stay exact
-      const int i = pq / (F::DS * N / 4);
-      const int e = (pq - i * (F::DS * N / 4)) * 4;
-      fv[u] = *reinterpret_cast<const f32x4*>(a.fn + ((int64_t)i * D + d0) * N + e);
+    for (int uu = 0; uu < F::FU; ++uu) {   // fn is 16-byte aligned (checked on the host)
+      const int u0 = tid + uu * kThreads;
+      const int u = u0 < F::PU ? u0 : F::PU - 1;   // no branch: the waits stay exact
+      const int g = u % F::NG, jq = u / F::NG;
+      const int j = jq >> 2, i = j / CPS, kk = j - i * CPS;
+      const float* src = a.fn + ((int64_t)i * D + d0 + kk * 32 + (jq & 3) * 8) * N + g * F::VW;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) fv[uu][e] = *reinterpret_cast<const FV*>(src + e * N);
     }
     __builtin_amdgcn_sched_barrier(0);
     // the first half of the first generation's residual columns goes out
@@ -214,41 +225,37 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
     // keep every load issued before the packing (the scheduler would sink the
     // residual loads towards their MFMAs and leave few loads in flight)
     __builtin_amdgcn_sched_barrier(0);
-    for (int i = 0; i < NS; ++i) {
-#pragma unroll
-      for (int u = 0; u < F::FP; ++u) {
-        const int pq = tid + u * kThreads;
-        if (pq < F::FQ && pq / (F::DS * N / 4) == i) {
-          const int e0 = (pq - i * (F::DS * N / 4)) * 4;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int r = (e0 + v) / N, c = e0 + v - r * N;
-            scratch[r * (N + 1) + c] = fv[u][v];
-          }
-        }
-      }
-      __syncthreads();
-      for (int f = tid; f < F::PER_STREAM * 64; f += kThreads) {
-        const int kk = f / (NCB * 64);
-        const int cb = (f / 64) % NCB;
-        const int l = f & 63;
-        const int col = cb * 16 + (l & 15);
-        const bool is_hi = col < N, is_lo = !is_hi && col < 2 * N;
-        const int c = is_hi ? col : col - N;
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float xv = (is_hi || is_lo) ? scratch[(kk * 32 + (l >> 4) * 8 + e) * (N + 1) + c] : 0.0f;
-          const float hi = (float)(__bf16)xv;
-          v[e] = is_hi ? hi : xv - hi;   // xv - hi is exact in fp32
-        }
-        u32x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
-        Bl[i * F::PER_STREAM * 64 + f] = o;
-      }
-      __syncthreads();
+    for (int z = tid; z < F::PZ; z += kThreads) {
+      const int jq = z / F::NPAD, col = 2 * N + NS + (z - jq * F::NPAD);
+      Bl[((jq >> 2) * NCB + col / 16) * 64 + (jq & 3) * 16 + (col & 15)] = u32x4{0u, 0u, 0u, 0u};
     }
+#pragma unroll
+    for (int uu = 0; uu < F::FU; ++uu) {
+      const int u = tid + uu * kThreads;
+      if (u < F::PU) {
+        const int g = u % F::NG, jq = u / F::NG;
+        u32x4* dst = Bl + (jq >> 2) * NCB * 64 + (jq & 3) * 16;
+#pragma unroll
+        for (int cc = 0; cc < F::VW; ++cc) {
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if constexpr (F::VW == 4) x[e] = fv[uu][e][cc];
+            else x[e] = fv[uu][e];
+          }
+          uint32_t hw[4], lw[4], l2w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) split3_pair(x[2 * e], x[2 * e + 1], hw[e], lw[e], l2w[e]);
+          const u32x4 h = {hw[0], hw[1], hw[2], hw[3]}, l = {lw[0], lw[1], lw[2], lw[3]};
+          const u32x4 l2 = {l2w[0], l2w[1], l2w[2], l2w[3]};
+          const int c = g * F::VW + cc;
+          dst[(c >> 4) * 64 + (c & 15)] = h;
+          dst[((N + c) >> 4) * 64 + ((N + c) & 15)] = l;
+          if (c < NS) dst[((2 * N + c) >> 4) * 64 + ((2 * N + c) & 15)] = l2;
+        }
+      }
+    }
+    __syncthreads();
   }
 
   load_cols(tile, std::integral_constant<int, kFirstCols>{}, std::integral_constant<int, CPS>{});
@@ -287,7 +294,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
 
-    // ---- 2. publish the partial rows of this wave's 16 tokens (hi + lo
+    // ---- 2. publish the partial rows of this wave's 16 tokens (hi + lo (+ lo2)
     // columns combined through this wave's part of the scratch)
     float* rw = scratch + w * (16 * CW);
 #pragma unroll
@@ -302,7 +309,8 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
       const int64_t tok = (int64_t)tile * kTM + w * 16 + r;
       if (tok < T) {
         const float* rr = rw + r * CW;
-        put_tagged(a.part + ((int64_t)sg * T + tok) * (N + 1) + c, tag, c < N ? rr[c] + rr[c + N] : rr[NCB * 16]);
+        const float v = c < NS ? rr[c] + rr[c + N] + rr[c + 2 * N] : (c < N ? rr[c] + rr[c + N] : rr[NCB * 16]);
+        put_tagged(a.part + ((int64_t)sg * T + tok) * (N + 1) + c, tag, v);
       }
     }
     __syncthreads();   // the scratch is reused below

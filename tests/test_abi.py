@@ -96,10 +96,10 @@ def test_pre_plan(L):
     assert L.mhc_pre_splits(1, 5, 8, 0, BF16) == UNSUPPORTED
     assert L.mhc_pre_workspace_bytes(0, 4, 64, 0, BF16) == 0
     assert L.mhc_pre_workspace_bytes(16, 5, 64, 0, BF16) == 0
-    # two-pass workspace: 256 B of status words, packed fn (K/32 k-steps x 3
+    # two-pass workspace: 256 B of status words, packed fn (K/32 k-steps x 4
     # column blocks x 1 KiB), partials [S, T, 28] fp32
     T, n, D = 2048, 4, 7168
-    fnp = (n * D // 32) * 3 * 1024
+    fnp = (n * D // 32) * 4 * 1024      # [hi | lo | lo2 of the 4 pre columns] = 52 -> 4 blocks of 16
     ws16 = L.mhc_pre_workspace_bytes(T, n, D, 16, BF16)
     assert L.mhc_pre_splits(T, n, D, 16, BF16) == 16
     assert ws16 == 256 + (fnp + 255) // 256 * 256 + (16 * T * 28 * 4 + 255) // 256 * 256

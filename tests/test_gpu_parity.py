@@ -89,12 +89,13 @@ def test_small_pre_post(T, n, D, dt, sp):
 
 
 # single-pass path: bf16 with D a multiple of 128 (tiles of 128 tokens, slices of 128)
-FUSED = [(1, 4, 512), (31, 4, 1024), (33, 4, 1536), (67, 3, 1024), (130, 2, 512), (17, 1, 2048), (64, 4, 5120),
-         (100, 4, 7168), (5, 4, 16384), (129, 4, 1056), (300, 3, 2240), (257, 2, 448)]
+SINGLE_PASS = [(1, 4, 512), (31, 4, 1024), (33, 4, 1536), (67, 3, 1024), (130, 2, 512), (17, 1, 2048), (64, 4, 5120),
+         (100, 4, 7168), (5, 4, 16384), (129, 4, 1056), (300, 3, 2240), (257, 2, 448),
+         (1100, 4, 7168)]   # the last: two generations of tiles, the second one ragged
 
 
-@pytest.mark.parametrize("T,n,D", FUSED, ids=lambda v: str(v))
-def test_fused_pre(T, n, D):
+@pytest.mark.parametrize("T,n,D", SINGLE_PASS, ids=lambda v: str(v))
+def test_single_pass_pre(T, n, D):
     S = mhc.mhc_pre_splits(T, n, D, -1, 0)
     assert S > 0 and D % S == 0 and (D // S) % 32 == 0
     assert mhc.mhc_pre_splits(T, n, D, 0, 0) == S   # the library's choice for bf16
@@ -120,7 +121,7 @@ def test_unaligned_fn(n_splits):
     assert e.value.status == -3
 
 
-def test_fused_matches_two_pass():
+def test_single_pass_matches_two_pass():
     x = W.generate(W.custom(96, 4, 4096, "bf16", seed=77))
     g = _gpu_inputs(x)
     a = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], n_splits=-1)
@@ -163,7 +164,7 @@ def test_workspace_reuse_across_shapes_and_paths():
         _compare_pre(x, outs, f"reuse call {i} T{T} D{D} splits {sp}")
 
 
-def test_fused_graph_replay():
+def test_single_pass_graph_replay():
     """The single-pass path captured in a HIP graph: every replay takes a new epoch from the
     workspace, so each replay (new inputs copied in between, eagerly) matches the oracle."""
     T, n, D = 200, 4, 7168
