@@ -12,10 +12,12 @@ the 256 MB Infinity Cache.
 Prints one JSON line: tokens/s (value), algorithmic HBM GB/s and its fraction
 of the 8 TB/s peak, a roofline object for the dominant kernel (algorithmic
 bytes per launch / average launch duration from HIP events recorded on the
-launch stream), and the CPU oracle timed on the host as a baseline.
+launch stream; the pre call, with the post call beside it as roofline_tail),
+and the CPU oracle timed on the host as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        python bench.py --summarize-rocprof DIR   (summarise rocprofv3 output)
+       python bench.py --write-traffic FETCH_DIR WRITE_DIR   (traffic profiles from two counter passes)
 """
 
 from __future__ import annotations
@@ -36,8 +38,15 @@ if ROOT not in sys.path:
 METRIC = "mhc_pre+post tokens/s and HBM GB/s (% of peak), T=2048 n=4 D=7168"
 PEAK_HBM_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-TRAFFIC_FILE = os.path.join(PROFILES, "traffic_post_prefill-d7168.txt")
-POST_SOURCE = os.path.join(ROOT, "mhc_hyper_connection_pre_amd", "csrc", "mhc_post.hip")
+CSRC = os.path.join(ROOT, "mhc_hyper_connection_pre_amd", "csrc")
+# Counter-derived HBM traffic per launch of the two kernels of the default
+# workload: the profile file and the sources its number holds for.
+TRAFFIC = {
+    "pre": ("traffic_pre_resident_prefill-d7168.txt", "pre_resident_kernel",
+            ["mhc_pre_resident.hip", "mhc_device.h", "mhc_pack.h", "mhc_epilogue.h", "mhc_internal.h"]),
+    "post": ("traffic_post_prefill-d7168.txt", "post_kernel<", ["mhc_post.hip", "mhc_device.h"]),
+}
+COPY_KIB = 1 << 20   # the 1 GiB calibration copy bench.py runs, in KiB read and written
 
 
 # ---------------------------------------------------------------- algorithmic bytes
@@ -61,26 +70,76 @@ def pcn_bytes(T, n, D, e):
 
 # ---------------------------------------------------------------- traffic from counters
 
-def source_hash(path=POST_SOURCE):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(which):
+    h = hashlib.sha256()
+    for name in TRAFFIC[which][2]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def stored_traffic():
-    """Counter-derived HBM bytes per post launch, if measured on the current kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def stored_traffic(which):
+    """Counter-derived HBM bytes per launch, if measured on the current kernel sources."""
+    path = os.path.join(PROFILES, TRAFFIC[which][0])
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != source_hash():
+    if vals.get("kernel_source_sha256_16") != source_hash(which):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def counter_values(d, counter):
+    """{kernel name: [value per dispatch]} for one counter from a rocprofv3 --pmc output directory."""
+    out = {}
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def write_traffic(fetch_dir, write_dir, command):
+    """Write the traffic profiles of the pre and post kernels from a FETCH_SIZE and a WRITE_SIZE pass over
+    the default bench run. Each counter is scaled by what it reads for the 1 GiB copy the same run makes
+    (the largest __amd_rocclr_copyBuffer dispatch)."""
+    fetch, write = counter_values(fetch_dir, "FETCH_SIZE"), counter_values(write_dir, "WRITE_SIZE")
+    copy = [k for k in fetch if "copyBuffer" in k]
+    if not copy:
+        raise SystemExit("no copy kernel in the FETCH_SIZE pass: cannot calibrate")
+    fs = COPY_KIB / max(fetch[copy[0]])
+    ws = COPY_KIB / max(write[copy[0]])
+    T, n, D, e = 2048, 4, 7168, 2
+    algo = {"pre": pre_bytes(T, n, D, e), "post": post_bytes(T, n, D, e)}
+    for which, (fname, key, sources) in TRAFFIC.items():
+        names = [k for k in fetch if key in k]
+        if not names or names[0] not in write:
+            raise SystemExit(f"kernel {key} missing from the counter passes")
+        k = names[0]
+        f_kib, w_kib = sum(fetch[k]) / len(fetch[k]), sum(write[k]) / len(write[k])
+        total = f_kib * 1024 * fs + w_kib * 1024 * ws
+        with open(os.path.join(PROFILES, fname), "w") as f:
+            f.write(f"# HBM traffic of {k}, prefill T=2048 n=4 D=7168 bf16, per launch\n")
+            f.write("# two rocprofv3 counter passes (one counter each), from the repository root on the MI355X box:\n")
+            for line in command:
+                f.write(f"#   {line}\n")
+            f.write(f"# calibration: the 1 GiB copy reads FETCH_SIZE {max(fetch[copy[0]]):.0f} KiB and WRITE_SIZE "
+                    f"{max(write[copy[0]]):.0f} KiB per dispatch: scales {fs:.5f} and {ws:.5f}\n")
+            f.write(f"# {len(fetch[k])} dispatches: FETCH_SIZE {f_kib:.1f} KiB = {f_kib * 1024 * fs / 1e6:.1f} MB read, "
+                    f"WRITE_SIZE {w_kib:.1f} KiB = {w_kib * 1024 * ws / 1e6:.1f} MB written\n")
+            f.write(f"# algorithmic bytes per launch: {algo[which]} ({algo[which] / 1e6:.1f} MB)\n")
+            f.write(f"# sources: {', '.join(sources)}\n")
+            f.write(f"kernel_source_sha256_16: {source_hash(which)}\n")
+            f.write(f"fetch_scale: {fs:.5f}\nwrite_scale: {ws:.5f}\n")
+            f.write(f"hbm_bytes_per_launch: {total:.0f}\n")
+        print(f"{fname}: {total / 1e6:.1f} MB per launch (algorithmic {algo[which] / 1e6:.1f} MB)")
 
 
 def summarize_rocprof(d):
@@ -271,7 +330,10 @@ def run(args):
     step_gbps = (bp + bq) / (ms_per_step * 1e-3) / 1e9
     post_gbps = bq / (post_ms * 1e-3) / 1e9
     pre_gbps = bp / (pre_ms * 1e-3) / 1e9
-    traffic = stored_traffic() if args.workload == W.THROUGHPUT_WORKLOAD else None
+    default_wl = args.workload == W.THROUGHPUT_WORKLOAD and spec.n_splits == W.spec(args.workload).n_splits
+    pre_kernel = ("pre_resident_kernel (mhc_pre, one launch)" if single
+                  else "mhc_pre (fn pack + split-K GEMM + epilogue launches)")
+    tail_kernel = "post_combine_norm_kernel" if fused_tail else "post_kernel (mhc_post)"
     result = {
         "metric": METRIC,
         "value": T / (ms_per_step * 1e-3),
@@ -299,10 +361,15 @@ def run(args):
         "copy_gbps_1GiB": copy_gbps,
         "hbm_frac_of_copy": step_gbps / copy_gbps,
         "tail": "mhc_post_combine_norm (fused, writes out too)" if fused_tail else "mhc_post",
-        "roofline": {"kernel": "post_combine_norm_kernel" if fused_tail else "post_kernel (mhc_post)",
-                     "bound": "hbm", "achieved": post_gbps,
-                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": post_gbps / PEAK_HBM_GBPS,
-                     "traffic": traffic, "algorithmic_bytes_per_launch": bq},
+        # the pre call is the longer of the two
+        "roofline": {"kernel": pre_kernel, "bound": "hbm", "achieved": pre_gbps,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": pre_gbps / PEAK_HBM_GBPS,
+                     "traffic": stored_traffic("pre") if default_wl and single else None,
+                     "algorithmic_bytes_per_launch": bp},
+        "roofline_tail": {"kernel": tail_kernel, "bound": "hbm", "achieved": post_gbps,
+                          "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": post_gbps / PEAK_HBM_GBPS,
+                          "traffic": stored_traffic("post") if default_wl and not fused_tail else None,
+                          "algorithmic_bytes_per_launch": bq},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
@@ -321,9 +388,16 @@ def main():
                     help="capture every call in a HIP graph and replay it (measured slower than direct launches here)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--summarize-rocprof", metavar="DIR")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the traffic profiles from a FETCH_SIZE and a WRITE_SIZE rocprofv3 pass")
+    ap.add_argument("--traffic-command", action="append", default=[],
+                    help="a line of the command that made the counter passes (recorded in the profile)")
     args = ap.parse_args()
     if args.summarize_rocprof:
         summarize_rocprof(args.summarize_rocprof)
+        return
+    if args.write_traffic:
+        write_traffic(*args.write_traffic, args.traffic_command)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: there is no multi-GPU path (every token is independent, so "

@@ -26,6 +26,13 @@ struct F32 {
 // 16-byte vector load / store through the vector memory path.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+// Streaming (non-temporal) store for outputs that no part of the same kernel
+// reads back: the lines do not stay dirty in L2 and the memory-side cache,
+// so neither the end-of-kernel L2 writeback nor the next kernel's reads pay
+// for writing them back later.
+__device__ __forceinline__ void st16_stream(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
 
 // bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 bits.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

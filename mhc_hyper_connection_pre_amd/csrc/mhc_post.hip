@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kPostThreads) void post_kernel(typename S::elem* __
           for (int i = 0; i < NS; ++i) a = fmaf(cij[i][j], xf[i][v], a);
           o[v] = a;
         }
-        st16(ot + j * D + c * V, Vec<S>::pack(o));
+        st16_stream(ot + j * D + c * V, Vec<S>::pack(o));
       }
     }
   }
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(1024) void post_combine_norm_kernel(
         o[v] = Vec<S>::round_trip(a);       // the stored post value
         cv[k][v] = fmaf(wj[j], o[v], cv[k][v]);
       }
-      if (out != nullptr) st16(out + (t * NS + j) * D + c * V, Vec<S>::pack(o));
+      if (out != nullptr) st16_stream(out + (t * NS + j) * D + c * V, Vec<S>::pack(o));
     }
 #pragma unroll
     for (int v = 0; v < V; ++v) {
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(1024) void post_combine_norm_kernel(
     float o[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) o[v] = (cv[k][v] * qn) * g[v];
-    st16(normalized + t * D + c * V, Vec<S>::pack(o));
+    st16_stream(normalized + t * D + c * V, Vec<S>::pack(o));
   }
 }
 

@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kEpiThreads) void pre_epilogue_kernel(
 #pragma unroll
       for (int v = 0; v < V; ++v) acc[v] = fmaf(p[i], f[v], acc[v]);
     }
-    st16(yt + c * V, Vec<S>::pack(acc));
+    st16_stream(yt + c * V, Vec<S>::pack(acc));
   };
 
 #pragma unroll

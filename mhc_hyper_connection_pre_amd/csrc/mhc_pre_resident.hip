@@ -427,7 +427,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
 #pragma unroll
           for (int v = 0; v < 8; ++v) o[v] = fmaf(pre[i], f[v], o[v]);
         }
-        if (rok) st16(yr + c * 32, Vec<BF16>::pack(o));
+        if (rok) st16_stream(yr + c * 32, Vec<BF16>::pack(o));
         if constexpr (NEXT) {
 #pragma unroll
           for (int i = 0; i < NS; ++i) {
