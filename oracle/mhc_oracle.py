@@ -40,8 +40,8 @@ a row normalisation followed by a column normalisation, so the last step
 always normalises columns; comb[i, j] weighs input stream i into output
 stream j.
 
-Parity status: pre_logits, gates, sinkhorn, mhc_pre, mhc_post and
-mhc_post_combine_norm are pinned by tests/test_oracle_pins.py (closed forms,
+Parity status: pre_logits, gates, sinkhorn, mhc_pre, mhc_post,
+mhc_post_combine_norm and mhc_post_pre are pinned by tests/test_oracle_pins.py (closed forms,
 invariants, exact rational arithmetic, brute force, library routines).
 The conventions listed above are readings; the pins check their
 self-consistency, not the pages.
@@ -375,3 +375,26 @@ def mhc_post_combine_norm(h, residual, post, comb, combine_w, norm_weight, *,
         out[sl] = encode(o, dtype)
         normalized[sl] = encode(rms_norm(c, g.astype(np.float64), norm_eps), dtype)
     return normalized, out
+
+
+# --------------------------------------------------------------------------
+# The layer boundary: mhc_post of the finished layer, then mhc_pre of the next.
+# --------------------------------------------------------------------------
+
+
+def mhc_post_pre(h, residual, post, comb, fn, hc_scale, bias, *, n: int, D: int, dtype: str,
+                 sinkhorn_repeat: int, eps: float, chunk: int = 1024):
+    """Layer boundary -> (out [T, n, D], post' [T, n] f32, comb' [T, n, n] f32, y' [T, D]).
+
+    [P1] section 2: a layer ends with the post call, whose result (shaped like
+    the residual) is the next layer's residual, and the next layer starts with
+    the pre call on it. [P2] section 1 fuses the post mix with the next
+    layer's input processing; this is the same boundary with the next layer's
+    full pre step. The definition is the two calls in sequence: out is
+    ``mhc_post`` rounded to the residual dtype, and ``mhc_pre`` reads that
+    stored value with the next layer's fn, hc_scale and bias.
+    """
+    out = mhc_post(h, residual, post, comb, n=n, D=D, dtype=dtype, chunk=chunk)
+    post_n, comb_n, y_n = mhc_pre(out, fn, hc_scale, bias, n=n, D=D, dtype=dtype,
+                                  sinkhorn_repeat=sinkhorn_repeat, eps=eps, chunk=chunk)
+    return out, post_n, comb_n, y_n

@@ -373,9 +373,47 @@ def pin_combine_reading_vs_float64(O):
     assert np.sqrt(np.mean(d ** 2)) < 2e-3 and np.mean(d > 2.0 ** -6) < 1e-3
 
 
+# ---------------------------------------------------------------- layer boundary (post, then the next pre)
+
+def pin_post_pre_boundary(O):
+    """Scalar loops for the post mix, the bf16 storage rounding and the next pre on the stored value; and
+    comb = I, post = 0 reduces the boundary to mhc_pre of the residual, bit for bit."""
+    g = np.random.default_rng(91)
+    R = 3
+    hc = np.array([1.0, 0.7, 1.3], np.float32)
+    for n in (1, 2, 3, 4):
+        T, D, N = 2, 8, n * (n + 2)
+        x = _bf16(g.standard_normal((T, n, D)))
+        h = _bf16(g.standard_normal((T, D)))
+        post = g.uniform(0, 1, (T, n)).astype(np.float32)
+        comb = g.uniform(0, 1, (T, n, n)).astype(np.float32)
+        fn = (g.standard_normal((n * D, N)) * 0.3).astype(np.float32)
+        bias = (g.standard_normal(N) * 0.3).astype(np.float32)
+        out, pn, cn, yn = O.mhc_post_pre(h, x, post, comb, fn, hc, bias, n=n, D=D, dtype="bf16",
+                                         sinkhorn_repeat=R, eps=EPS)
+        xv, hv = _bf16_val(x), _bf16_val(h)
+        for t in range(T):
+            o = B.post_token(hv[t].tolist(), xv[t].tolist(), post[t].astype(np.float64).tolist(),
+                             comb[t].astype(np.float64).tolist(), n, D)
+            ob = [[B.bf16(v) for v in row] for row in o]
+            assert np.array_equal(_bf16_val(out[t]), np.array(ob)), f"boundary out n={n} t={t}"
+            b = B.pre_token(ob, fn.astype(np.float64).tolist(), hc.astype(np.float64).tolist(),
+                            bias.astype(np.float64).tolist(), n, D, R, EPS)
+            _close(pn[t], [B.f32(v) for v in b["post"]], rtol=2.0 ** -23, atol=0, what=f"boundary post' n={n}")
+            _close(cn[t], [[B.f32(v) for v in row] for row in b["comb"]], rtol=2.0 ** -23, atol=1e-30,
+                   what=f"boundary comb' n={n}")
+            _close(_bf16_val(yn[t]), [B.bf16(v) for v in b["y"]], rtol=2.0 ** -8, atol=0, what=f"boundary y' n={n}")
+        eye = np.broadcast_to(np.eye(n, dtype=np.float32), (T, n, n)).copy()
+        out, pn, cn, yn = O.mhc_post_pre(h, x, np.zeros((T, n), np.float32), eye, fn, hc, bias, n=n, D=D,
+                                         dtype="bf16", sinkhorn_repeat=R, eps=EPS)
+        p0, c0, y0 = O.mhc_pre(x, fn, hc, bias, n=n, D=D, dtype="bf16", sinkhorn_repeat=R, eps=EPS)
+        assert np.array_equal(out, x) and np.array_equal(pn, p0) and np.array_equal(cn, c0)
+        assert np.array_equal(yn, y0)
+
+
 ALL_PINS = [
     pin_brute_pre, pin_brute_post, pin_rounding, pin_rms_closed_form, pin_gemm_onehot_and_groups,
     pin_gates, pin_sinkhorn_exact, pin_sinkhorn_closed_forms, pin_sinkhorn_invariants,
     pin_pre_special_cases, pin_permutation_equivariance, pin_stored_outputs, pin_post_identities,
-    pin_post_orientation, pin_combine_norm, pin_combine_reading_vs_float64,
+    pin_post_orientation, pin_combine_norm, pin_combine_reading_vs_float64, pin_post_pre_boundary,
 ]

@@ -8,7 +8,7 @@ from oracle_pins import ALL_PINS
 
 _orig = {k: getattr(O, k) for k in ("pre_logits", "gates", "sinkhorn", "post_mix", "stream_reduce",
                                     "rms_norm", "f64_to_bf16_bits", "logit_groups", "mhc_post_combine_norm",
-                                    "combine_intermediates")}
+                                    "combine_intermediates", "mhc_post_pre", "mhc_pre", "mhc_post", "encode")}
 
 
 def _sinkhorn_cols_first(Z, repeat):
@@ -117,7 +117,26 @@ def _combine_weights_reversed(h, x, post, comb, w, dtype):
     return _orig["combine_intermediates"](h, x, post, comb, np.asarray(w)[:, ::-1], dtype)
 
 
+def _boundary_pre_on_old_residual(h, residual, post, comb, fn, hc_scale, bias, *, n, D, dtype, sinkhorn_repeat,
+                                  eps, chunk=1024):
+    out = _orig["mhc_post"](h, residual, post, comb, n=n, D=D, dtype=dtype)
+    return (out,) + _orig["mhc_pre"](residual, fn, hc_scale, bias, n=n, D=D, dtype=dtype,
+                                     sinkhorn_repeat=sinkhorn_repeat, eps=eps)
+
+
+def _boundary_pre_on_unrounded(h, residual, post, comb, fn, hc_scale, bias, *, n, D, dtype, sinkhorn_repeat,
+                               eps, chunk=1024):
+    out = _orig["mhc_post"](h, residual, post, comb, n=n, D=D, dtype=dtype)
+    mix = O.post_mix(O.decode(h, dtype), O.decode(residual, dtype), np.asarray(post, np.float64),
+                     np.asarray(comb, np.float64)).astype(np.float32)
+    pn, cn, yn = _orig["mhc_pre"](mix, fn, hc_scale, bias, n=n, D=D, dtype="f32", sinkhorn_repeat=sinkhorn_repeat,
+                                  eps=eps)
+    return out, pn, cn, _orig["encode"](yn.astype(np.float64), dtype)
+
+
 MUTATIONS = {
+    "boundary pre reads the finished layer's residual": ("mhc_post_pre", _boundary_pre_on_old_residual),
+    "boundary pre reads the post mix before storage rounding": ("mhc_post_pre", _boundary_pre_on_unrounded),
     "combined row kept unrounded": ("combine_intermediates", _combine_c_unrounded),
     "combine weights applied to the wrong streams": ("combine_intermediates", _combine_weights_reversed),
     "sinkhorn columns first": ("sinkhorn", _sinkhorn_cols_first),
