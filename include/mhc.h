@@ -68,9 +68,9 @@ MHC_API const char* mhc_last_error(void);
  * negative status for arguments mhc_pre would reject. */
 MHC_API int mhc_pre_splits(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt);
 
-/* Bytes of device workspace mhc_pre needs for these sizes and knobs (0 when
- * T = 0; a conservative positive value for arguments it would reject is
- * never returned - it returns 0 and mhc_pre reports the error). */
+/* Bytes of device workspace mhc_pre and mhc_post_pre need for these sizes and
+ * knobs (0 when T = 0, and 0 for arguments mhc_pre would reject: the call
+ * itself then reports the error). One workspace of this size serves both. */
 MHC_API size_t mhc_pre_workspace_bytes(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt);
 
 /*
@@ -94,13 +94,18 @@ MHC_API size_t mhc_pre_workspace_bytes(int64_t T, int n, int64_t D, int n_splits
  *   residual dt [T, n, D]; fn float32 [n*D, N]; hc_scale float32 [3]
  *   (pre, post, comb); bias float32 [N].
  * Knobs: sinkhorn_repeat >= 1; eps > 0; n_splits = split-K partials over the
- *   hidden axis (0 = library choice, else 1..256; any value gives the same
- *   result up to fp32 reassociation, and a fixed value is bitwise repeatable).
- * Paths: bf16 with D a multiple of 128 (D <= 16384) and n_splits = D / 128
- *   runs the single-pass kernel (the residual is read once; the workgroups
- *   of a token tile exchange partial sums through the workspace); any other
- *   call runs the two-pass path (pack fn, split-K GEMM, then an epilogue that
- *   reads the residual again for y).
+ *   hidden axis: 0 = library choice; 1..256 = that many partials on the
+ *   two-pass path; -1 = the single-pass path or an error (MHC_ERR_UNSUPPORTED
+ *   for a shape it does not cover, MHC_ERR_MISALIGNED for an fn that is not
+ *   16-byte aligned). Any value gives the same result up to fp32
+ *   reassociation, and a fixed value is bitwise repeatable.
+ * Paths: the single-pass kernel (one launch; the residual is read once and
+ *   stays in registers; the workgroups of a token tile exchange partial sums
+ *   through the workspace) covers bf16 with D a multiple of 32 for which a
+ *   slice tiling fits (mhc_pre_splits(..., -1, ...) > 0) and a 16-byte
+ *   aligned fn; n_splits = 0 takes it when it can. Otherwise the two-pass
+ *   path runs (pack fn, split-K GEMM, then an epilogue that reads the
+ *   residual again for y).
  * Workspace: device memory of at least mhc_pre_workspace_bytes(...) bytes,
  *   256-byte aligned, owned by the caller, not shared by concurrent calls.
  *   Its first 256 bytes are status words that the single-pass path keeps
@@ -138,6 +143,40 @@ MHC_API int mhc_pre_sync_timeouts(const void* workspace, size_t workspace_bytes,
 MHC_API int mhc_post(void* out, const void* h, const void* residual,
                      const float* post, const float* comb, mhc_dtype dt,
                      int64_t T, int n, int64_t D, void* stream);
+
+/*
+ * mhc_post_pre - the layer boundary: mhc_post of the finished layer, then
+ * mhc_pre of the next layer on its result. [P1] section 2: a layer ends with
+ * the post call, whose result (shaped like the residual) is the next
+ * layer's residual, and the next layer begins with the pre call on it; [P2]
+ * section 1 fuses the post mix with the next layer's input processing to
+ * save memory traffic, and the closing paragraph of [P2] names that saving.
+ *   out                       = mhc_post(h, residual, post, comb), rounded to dt
+ *   post_next, comb_next, y_next = mhc_pre(out, fn, hc_scale, bias, ...)
+ * exactly as the two calls in sequence (the same bits as mhc_post followed by
+ * mhc_pre with the same knobs, when both run the same pre path).
+ * Outputs: out dt [T, n, D] (must not overlap residual or h: else
+ *   MHC_ERR_INVALID_ARG); post_next float32 [T, n]; comb_next float32
+ *   [T, n, n]; y_next dt [T, D].
+ * Inputs: h, residual, post, comb as mhc_post (post and comb of the finished
+ *   layer); fn, hc_scale, bias of the next layer as mhc_pre.
+ * Knobs, workspace and errors: as mhc_pre (same workspace size and status
+ *   words). When the single-pass kernel covers the shape (see
+ *   mhc_post_pre_fused) the call is one launch that reads h and the residual
+ *   once, forms out in registers, writes out and y_next, and never reads out
+ *   back; otherwise it launches mhc_post's kernel and then mhc_pre's path on
+ *   out.
+ */
+MHC_API int mhc_post_pre(void* out, float* post_next, float* comb_next, void* y_next,
+                         const void* h, const void* residual, const float* post, const float* comb,
+                         mhc_dtype dt, const float* fn, const float* hc_scale, const float* bias,
+                         int64_t T, int n, int64_t D, int sinkhorn_repeat, float eps, int n_splits,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* 1 if mhc_post_pre runs as one launch for these sizes and knobs (given a
+ * 16-byte aligned fn), 0 if it runs mhc_post and mhc_pre's kernels in
+ * sequence, or a negative status for arguments it would reject. */
+MHC_API int mhc_post_pre_fused(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt);
 
 /*
  * mhc_post_combine_norm - [P2] section 1 (post mix, combine into one bf16

@@ -8,7 +8,9 @@ pointers and the current HIP stream. There is no CPU fallback: if the library
 is not built, every call raises.
 
 Functions mirror the C entry points: ``mhc_pre``, ``mhc_post``,
-``mhc_post_combine_norm``, ``mhc_pre_workspace_bytes``, ``mhc_pre_splits``.
+``mhc_post_combine_norm``, ``mhc_post_pre`` (the layer boundary: post, then
+the next layer's pre), ``mhc_pre_workspace_bytes``, ``mhc_pre_splits``,
+``mhc_post_pre_fused``.
 """
 
 from __future__ import annotations
@@ -18,7 +20,8 @@ import os
 
 __all__ = [
     "MhcError", "lib", "library_path", "mhc_pre", "mhc_post", "mhc_post_combine_norm",
-    "mhc_pre_workspace_bytes", "mhc_pre_splits", "mhc_pre_sync_timeouts", "MHC_BF16", "MHC_F32",
+    "mhc_pre_workspace_bytes", "mhc_pre_splits", "mhc_pre_sync_timeouts", "mhc_post_pre", "mhc_post_pre_fused",
+    "MHC_BF16", "MHC_F32",
 ]
 
 MHC_BF16 = 0
@@ -70,6 +73,10 @@ def lib() -> ctypes.CDLL:
     L.mhc_post.restype = I
     L.mhc_post_combine_norm.argtypes = [P, P, P, P, P, P, P, P, F, I, I64, I, I64, P]
     L.mhc_post_combine_norm.restype = I
+    L.mhc_post_pre.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, I64, I, I64, I, F, I, P, SZ, P]
+    L.mhc_post_pre.restype = I
+    L.mhc_post_pre_fused.argtypes = [I64, I, I64, I, I]
+    L.mhc_post_pre_fused.restype = I
     _LIB = L
     return L
 
@@ -209,3 +216,48 @@ def mhc_post_combine_norm(h, residual, post, comb, combine_w, norm_weight, *, no
     if st != 0:
         raise MhcError("mhc_post_combine_norm", st)
     return normalized, out
+
+
+def mhc_post_pre_fused(T: int, n: int, D: int, n_splits: int = 0, dtype_code: int = MHC_BF16) -> bool:
+    """True if mhc_post_pre runs as one launch for these sizes (with a 16-byte aligned fn)."""
+    st = lib().mhc_post_pre_fused(T, n, D, n_splits, dtype_code)
+    if st < 0:
+        raise MhcError("mhc_post_pre_fused", st)
+    return bool(st)
+
+
+def mhc_post_pre(h, residual, post, comb, fn, hc_scale, bias, *, sinkhorn_repeat: int = 20, eps: float = 1e-6,
+                 n_splits: int = 0, out=None, post_next=None, comb_next=None, y=None, workspace=None, stream=None):
+    """(out [T, n, D], post' [T, n], comb' [T, n, n], y' [T, D]): mhc_post of the finished layer, then the
+    next layer's mhc_pre (fn, hc_scale, bias) on its result."""
+    torch = _torch()
+    L = lib()
+    T, n, D = residual.shape
+    dev = residual.device
+    dt = _dtype_code(residual)
+    N = n * (n + 2)
+    _check(h, (T, D), residual.dtype, dev, "h")
+    _check(residual, (T, n, D), residual.dtype, dev, "residual")
+    _check(post, (T, n), torch.float32, dev, "post")
+    _check(comb, (T, n, n), torch.float32, dev, "comb")
+    _check(fn, (n * D, N), torch.float32, dev, "fn")
+    _check(hc_scale, (3,), torch.float32, dev, "hc_scale")
+    _check(bias, (N,), torch.float32, dev, "bias")
+    out = torch.empty_like(residual) if out is None else out
+    post_next = torch.empty((T, n), dtype=torch.float32, device=dev) if post_next is None else post_next
+    comb_next = torch.empty((T, n, n), dtype=torch.float32, device=dev) if comb_next is None else comb_next
+    y = torch.empty((T, D), dtype=residual.dtype, device=dev) if y is None else y
+    _check(out, (T, n, D), residual.dtype, dev, "out")
+    _check(post_next, (T, n), torch.float32, dev, "post_next")
+    _check(comb_next, (T, n, n), torch.float32, dev, "comb_next")
+    _check(y, (T, D), residual.dtype, dev, "y")
+    need = L.mhc_pre_workspace_bytes(T, n, D, n_splits, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        workspace[:256].zero_()
+    st = L.mhc_post_pre(_ptr(out), _ptr(post_next), _ptr(comb_next), _ptr(y), _ptr(h), _ptr(residual), _ptr(post),
+                        _ptr(comb), dt, _ptr(fn), _ptr(hc_scale), _ptr(bias), T, n, D, sinkhorn_repeat, eps,
+                        n_splits, _ptr(workspace), workspace.numel(), _stream(dev, stream))
+    if st != 0:
+        raise MhcError("mhc_post_pre", st)
+    return out, post_next, comb_next, y

@@ -39,7 +39,7 @@ int check_shape(int64_t T, int n, int64_t D, mhc_dtype dt) {
 
 }  // namespace
 
-int make_pre_plan(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, PrePlan* p) {
+int make_pre_plan(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, PrePlan* p, bool boundary) {
   int st = check_shape(T, n, D, dt);
   if (st != MHC_OK) return st;
   if (n_splits < kSplitsSinglePass || n_splits > 256) return MHC_ERR_INVALID_ARG;
@@ -92,7 +92,7 @@ int make_pre_plan(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, PrePl
   // request (n_splits = -1). Layout: status, packed fn (as above), then the
   // tagged exchange words: partials [rS][T][N + 1] and pre [T][4], 8 bytes each.
   ResidentChoice rc{};
-  const bool res_ok = n_splits <= 0 && resident_choose(T, n, D, dt, &rc);
+  const bool res_ok = n_splits <= 0 && resident_choose(T, n, D, dt, &rc, boundary);
   if (n_splits == kSplitsSinglePass && !res_ok) return MHC_ERR_UNSUPPORTED;
   q.res = res_ok;
   q.total_bytes = total2;
@@ -111,6 +111,40 @@ int make_pre_plan(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, PrePl
   *p = q;
   return MHC_OK;
 }
+
+namespace {
+
+// The pre step once the plan is made and the arguments are checked.
+int run_pre(const PrePlan& p, float* post, float* comb, void* y, const void* residual, const float* fn,
+            const float* hc_scale, const float* bias, int sinkhorn_repeat, float eps, void* workspace,
+            hipStream_t s) {
+  hipError_t e;
+  if (p.res && aligned(fn, 16)) {
+    e = launch_pre_resident(p, residual, fn, hc_scale, bias, post, comb, y, workspace, sinkhorn_repeat, eps, s);
+    return e == hipSuccess ? MHC_OK : hip_fail(e);
+  }
+  // Two-pass path.
+  char* ws = static_cast<char*>(workspace);
+  float* part = reinterpret_cast<float*>(ws + p.off_part);
+  void* fnp = ws + p.off_fnp;
+  if (p.dt == MHC_BF16) {
+    e = launch_pack_fn(p, fn, fnp, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  e = launch_pre_gemm(p, residual, fnp, fn, part, s);
+  if (e != hipSuccess) return hip_fail(e);
+  e = launch_pre_epilogue(p, residual, part, hc_scale, bias, post, comb, y, sinkhorn_repeat, eps,
+                          reinterpret_cast<unsigned long long*>(ws), s);
+  if (e != hipSuccess) return hip_fail(e);
+  return MHC_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+}  // namespace
 
 }  // namespace mhc
 
@@ -139,9 +173,17 @@ MHC_API int mhc_pre_splits(int64_t T, int n, int64_t D, int n_splits, mhc_dtype 
 }
 
 MHC_API size_t mhc_pre_workspace_bytes(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt) {
-  PrePlan p;
+  PrePlan p, q;
   if (T == 0 || make_pre_plan(T, n, D, n_splits, dt, &p) != MHC_OK) return 0;
+  // the same workspace serves mhc_post_pre, whose single-pass tiling may differ
+  if (make_pre_plan(T, n, D, n_splits, dt, &q, true) == MHC_OK && q.total_bytes > p.total_bytes) return q.total_bytes;
   return p.total_bytes;
+}
+
+MHC_API int mhc_post_pre_fused(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt) {
+  PrePlan p;
+  const int st = make_pre_plan(T, n, D, n_splits, dt, &p, true);
+  return st != MHC_OK ? st : (p.res ? 1 : 0);
 }
 
 MHC_API int mhc_pre(float* post, float* comb, void* y, const void* residual, mhc_dtype dt, const float* fn,
@@ -157,27 +199,46 @@ MHC_API int mhc_pre(float* post, float* comb, void* y, const void* residual, mhc
   if (!aligned(post, 4) || !aligned(comb, 4) || !aligned(fn, 4) || !aligned(hc_scale, 4) || !aligned(bias, 4))
     return MHC_ERR_MISALIGNED;
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.total_bytes) return MHC_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
   if (p.res && !aligned(fn, 16) && n_splits == kSplitsSinglePass) return MHC_ERR_MISALIGNED;
-  if (p.res && aligned(fn, 16)) {
-    e = launch_pre_resident(p, residual, fn, hc_scale, bias, post, comb, y, workspace, sinkhorn_repeat, eps, s);
-    return e == hipSuccess ? MHC_OK : hip_fail(e);
+  return run_pre(p, post, comb, y, residual, fn, hc_scale, bias, sinkhorn_repeat, eps, workspace,
+                 static_cast<hipStream_t>(stream));
+}
+
+MHC_API int mhc_post_pre(void* out, float* post_next, float* comb_next, void* y_next, const void* h,
+                         const void* residual, const float* post, const float* comb, mhc_dtype dt, const float* fn,
+                         const float* hc_scale, const float* bias, int64_t T, int n, int64_t D, int sinkhorn_repeat,
+                         float eps, int n_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  PrePlan fp, pp;
+  int st = make_pre_plan(T, n, D, n_splits, dt, &fp, true);
+  if (st != MHC_OK) return st;
+  st = make_pre_plan(T, n, D, n_splits, dt, &pp);
+  if (st != MHC_OK) return st;
+  if (sinkhorn_repeat < 1 || !(eps > 0.0f) || !std::isfinite(eps)) return MHC_ERR_INVALID_ARG;
+  if (T == 0) return MHC_OK;
+  if (!out || !post_next || !comb_next || !y_next || !h || !residual || !post || !comb || !fn || !hc_scale || !bias)
+    return MHC_ERR_INVALID_ARG;
+  const size_t e = dt == MHC_BF16 ? 2 : 4;
+  const size_t res_bytes = (size_t)T * n * D * e;
+  if (overlaps(out, res_bytes, residual, res_bytes) || overlaps(out, res_bytes, h, (size_t)T * D * e))
+    return MHC_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(h, 16) || !aligned(residual, 16) || !aligned(y_next, 16))
+    return MHC_ERR_MISALIGNED;
+  if (!aligned(post_next, 4) || !aligned(comb_next, 4) || !aligned(post, 4) || !aligned(comb, 4) ||
+      !aligned(fn, 4) || !aligned(hc_scale, 4) || !aligned(bias, 4))
+    return MHC_ERR_MISALIGNED;
+  const size_t need = fp.total_bytes > pp.total_bytes ? fp.total_bytes : pp.total_bytes;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return MHC_ERR_WORKSPACE;
+  if (fp.res && !aligned(fn, 16) && n_splits == kSplitsSinglePass) return MHC_ERR_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fp.res && aligned(fn, 16)) {
+    const hipError_t er = launch_post_pre_resident(fp, h, residual, post, comb, out, fn, hc_scale, bias, post_next,
+                                                   comb_next, y_next, workspace, sinkhorn_repeat, eps, s);
+    return er == hipSuccess ? MHC_OK : hip_fail(er);
   }
-  // Two-pass path.
-  char* ws = static_cast<char*>(workspace);
-  float* part = reinterpret_cast<float*>(ws + p.off_part);
-  void* fnp = ws + p.off_fnp;
-  if (dt == MHC_BF16) {
-    e = launch_pack_fn(p, fn, fnp, s);
-    if (e != hipSuccess) return hip_fail(e);
-  }
-  e = launch_pre_gemm(p, residual, fnp, fn, part, s);
-  if (e != hipSuccess) return hip_fail(e);
-  e = launch_pre_epilogue(p, residual, part, hc_scale, bias, post, comb, y, sinkhorn_repeat, eps,
-                          reinterpret_cast<unsigned long long*>(ws), s);
-  if (e != hipSuccess) return hip_fail(e);
-  return MHC_OK;
+  // the two calls in sequence
+  const hipError_t er = launch_post(h, residual, post, comb, out, dt, T, n, D, s);
+  if (er != hipSuccess) return hip_fail(er);
+  return run_pre(pp, post_next, comb_next, y_next, out, fn, hc_scale, bias, sinkhorn_repeat, eps, workspace, s);
 }
 
 MHC_API int mhc_pre_sync_timeouts(const void* workspace, size_t workspace_bytes, int64_t T, int n, int64_t D,

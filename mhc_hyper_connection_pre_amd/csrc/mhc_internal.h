@@ -47,7 +47,9 @@ constexpr int kStArrive = 24;   // first-use barrier arrivals of the running cal
 constexpr int kSplitsSinglePass = -1;
 
 // Fills `p`; returns MHC_OK or the status mhc_pre would return for the sizes.
-int make_pre_plan(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, PrePlan* p);
+// boundary: plan the layer-boundary call (mhc_post_pre), whose single-pass
+// kernel also keeps the block output in registers.
+int make_pre_plan(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, PrePlan* p, bool boundary = false);
 
 // Launchers (stream-ordered, no synchronisation). Return the launch error.
 hipError_t launch_pack_fn(const PrePlan& p, const float* fn, void* fnp, hipStream_t s);
@@ -59,12 +61,18 @@ hipError_t launch_pre_epilogue(const PrePlan& p, const void* residual, const flo
 hipError_t launch_pre_resident(const PrePlan& p, const void* residual, const float* fn, const float* hc_scale,
                                const float* bias, float* post, float* comb, void* y, void* workspace, int repeat,
                                float eps, hipStream_t s);
+// The same kernel at the layer boundary: out = mhc_post(h, residual, post_in,
+// comb_in) is formed in registers, stored, and is the residual of the pre step.
+hipError_t launch_post_pre_resident(const PrePlan& p, const void* h, const void* residual, const float* post_in,
+                                    const float* comb_in, void* out, const float* fn, const float* hc_scale,
+                                    const float* bias, float* post, float* comb, void* y, void* workspace,
+                                    int repeat, float eps, hipStream_t s);
 // Single-pass tiling for the shape on the current device (or a 256-CU MI355X
 // when no device is visible): false if the shape is not supported.
 struct ResidentChoice {
   int cps, S, per, TB;
 };
-bool resident_choose(int64_t T, int n, int64_t D, mhc_dtype dt, ResidentChoice* c);
+bool resident_choose(int64_t T, int n, int64_t D, mhc_dtype dt, ResidentChoice* c, bool boundary = false);
 constexpr int kResidentTile = 128;
 
 hipError_t launch_post(const void* h, const void* residual, const float* post, const float* comb,

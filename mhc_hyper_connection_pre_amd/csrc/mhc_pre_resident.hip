@@ -63,6 +63,7 @@ constexpr int kTM = kResidentTile;        // 128 tokens per tile
 constexpr int kLoads = 8;                 // partial words per thread per finalise batch
 constexpr int kMaxSplits = 16 * kLoads;   // 16 thread groups x kLoads words cover a token's splits
 constexpr int kMaxAVgprs = 128;           // residual registers per wave
+constexpr int kMaxAVgprsPost = 144;       // residual + block-output registers (layer boundary)
 constexpr int kLdsMax = 160 * 1024;
 constexpr long long kPollTicks = 10000000LL;  // 100 ms of the 100 MHz wall clock
 constexpr int kCpsList[] = {1, 2, 4, 5, 7, 8, 14};
@@ -108,6 +109,12 @@ struct ResArgs {
   int64_t T, D;
   int S, G, P, TB, repeat;
   float eps, K;
+  // layer boundary only: x is the finished layer's residual, and the pre step
+  // runs on out = mhc_post(h, x, post_in, comb_in), which is also stored
+  const uint16_t* h;
+  const float* post_in;
+  const float* comb_in;
+  uint16_t* out;
 };
 
 template <int NS, int CPS>
@@ -132,9 +139,12 @@ struct ResShape {
   static constexpr int NPAD = NCB * 16 - (2 * N + NS);   // zero columns past lo2
   static constexpr int PZ = KSW * 4 * NPAD;
   static constexpr bool fits = 4 * KSW <= kMaxAVgprs && lds_bytes <= (size_t)kLdsMax;
+  static constexpr bool fits_post = 4 * KSW + 4 * CPS <= kMaxAVgprsPost && lds_bytes <= (size_t)kLdsMax;
 };
 
-template <int NS, int CPS>
+// POST: the layer boundary (mhc_post of the finished layer, then this pre on
+// its result); the GEMM's A operand is the post mix formed in registers.
+template <int NS, int CPS, bool POST>
 __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
   typedef ResShape<NS, CPS> F;
   constexpr int N = F::N, NCB = F::NCB, CW = F::CW, KSW = F::KSW;
@@ -180,20 +190,42 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
 
   int tile = (int)(blockIdx.x / S);
   u32x4 A[KSW];
+  u32x4 H[POST ? CPS : 1];            // layer boundary: block-output columns of the tile
+  float pw[POST ? NS + NS * NS : 1];  // layer boundary: post and comb of this lane's token
   // Residual slice of tile t (rows past T read row 0 and are never published
-  // or stored), issued column by column (k-step c of every stream), the order
-  // in which y frees the registers and the GEMM consumes them.
+  // or stored), issued column by column (k-step c of every stream, then the
+  // block output's column c at the layer boundary), the order in which y
+  // frees the registers and the GEMM consumes them.
   auto load_cols = [&](int t, auto c0_tag, auto c1_tag) {
     constexpr int C0 = decltype(c0_tag)::value, C1 = decltype(c1_tag)::value;
     const int64_t rw0 = (int64_t)t * kTM + w * 16 + r16;
-    const uint16_t* xr = a.x + (rw0 < T ? rw0 : 0) * NS * D + d0 + q * 8;
+    const int64_t rr = rw0 < T ? rw0 : 0;
+    const uint16_t* xr = a.x + rr * NS * D + d0 + q * 8;
 #pragma unroll
-    for (int c = C0; c < C1; ++c)
+    for (int c = C0; c < C1; ++c) {
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         A[i * CPS + c] = ld16(xr + i * D + c * 32);
         __builtin_amdgcn_sched_barrier(0);   // issue in exactly this order (the waits depend on it)
       }
+      if constexpr (POST) {
+        H[c] = ld16(a.h + rr * D + d0 + q * 8 + c * 32);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  // layer boundary: post and comb of the finished layer for this lane's token
+  // of tile t, issued ahead of the tile's residual
+  auto load_pw = [&](int t) {
+    if constexpr (POST) {
+      const int64_t rw0 = (int64_t)t * kTM + w * 16 + r16;
+      const int64_t rr = rw0 < T ? rw0 : 0;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) pw[j] = a.post_in[rr * NS + j];
+#pragma unroll
+      for (int k = 0; k < NS * NS; ++k) pw[NS + k] = a.comb_in[rr * NS * NS + k];
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   // ---- 0. fn slice -> B fragments in LDS (once). Fragment
@@ -217,6 +249,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
       for (int e = 0; e < 8; ++e) fv[uu][e] = *reinterpret_cast<const FV*>(src + e * N);
     }
     __builtin_amdgcn_sched_barrier(0);
+    load_pw(tile);
     // the first half of the first generation's residual columns goes out
     // right behind the fn slice (HBM stays busy while B is packed), the rest
     // once B is in LDS (with all of it queued at once, the whole chip's
@@ -276,7 +309,38 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
     for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float ss = 0.0f;
 #pragma unroll
-    for (int c = 0; c < CPS; ++c)   // the load order
+    for (int c = 0; c < CPS; ++c) {   // the load order
+      if constexpr (POST) {
+        // column c of the new residual, out_j = post_j h + sum_i comb[i][j]
+        // x_i, in fp32 with the operation order and the single rounding of
+        // mhc_post; stored, then the GEMM's A operand in place of x_j
+        u32x4 ov[NS];
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+          const float h0 = bf16_lo(H[c][wd]), h1 = bf16_hi(H[c][wd]);
+          float x0[NS], x1[NS];
+#pragma unroll
+          for (int i = 0; i < NS; ++i) {
+            x0[i] = bf16_lo(A[i * CPS + c][wd]);
+            x1[i] = bf16_hi(A[i * CPS + c][wd]);
+          }
+#pragma unroll
+          for (int jj = 0; jj < NS; ++jj) {
+            float o0 = pw[jj] * h0, o1 = pw[jj] * h1;
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+              o0 = fmaf(pw[NS + i * NS + jj], x0[i], o0);
+              o1 = fmaf(pw[NS + i * NS + jj], x1[i], o1);
+            }
+            ov[jj][wd] = pack_bf16x2(o0, o1);
+          }
+        }
+#pragma unroll
+        for (int jj = 0; jj < NS; ++jj) {
+          A[jj * CPS + c] = ov[jj];
+          if (rok) st16_stream(a.out + row * NS * D + jj * D + d0 + q * 8 + c * 32, ov[jj]);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         const int j = i * CPS + c;
@@ -291,6 +355,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
         ss = dot2_self(aw.z, ss);
         ss = dot2_self(aw.w, ss);
       }
+    }
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
 
@@ -414,7 +479,9 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
     {
       uint16_t* yr = a.y + row * D + d0 + q * 8;
       const int64_t nrow = (int64_t)(tile + G) * kTM + w * 16 + r16;
-      const uint16_t* nxr = a.x + (nrow < T ? nrow : 0) * NS * D + d0 + q * 8;
+      const int64_t nrr = nrow < T ? nrow : 0;
+      const uint16_t* nxr = a.x + nrr * NS * D + d0 + q * 8;
+      if constexpr (NEXT) load_pw(tile + G);
 #pragma unroll
       for (int c = 0; c < CPS; ++c) {
         float o[8], f[8];
@@ -432,6 +499,10 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
 #pragma unroll
           for (int i = 0; i < NS; ++i) {
             A[i * CPS + c] = ld16(nxr + i * D + c * 32);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if constexpr (POST) {
+            H[c] = ld16(a.h + nrr * D + d0 + q * 8 + c * 32);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -456,28 +527,28 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
 
 namespace {
 
-template <int NS, int CPS>
+template <int NS, int CPS, bool POST>
 int occupancy_of() {
   typedef ResShape<NS, CPS> F;
-  if constexpr (!F::fits) {
+  if constexpr (!(POST ? F::fits_post : F::fits)) {
     return 0;
   } else {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(pre_resident_kernel<NS, CPS>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(pre_resident_kernel<NS, CPS, POST>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)F::lds_bytes) != hipSuccess)
       return -1;
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, pre_resident_kernel<NS, CPS>, kThreads, F::lds_bytes) !=
-        hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, pre_resident_kernel<NS, CPS, POST>, kThreads,
+                                                     F::lds_bytes) != hipSuccess)
       return -1;
     return occ;
   }
 }
 
-template <int NS, int CPS>
+template <int NS, int CPS, bool POST>
 void launch_one(const ResArgs& a, unsigned grid, hipStream_t s) {
   typedef ResShape<NS, CPS> F;
-  if constexpr (F::fits)
-    hipLaunchKernelGGL((pre_resident_kernel<NS, CPS>), dim3(grid), dim3(kThreads), F::lds_bytes, s, a);
+  if constexpr (POST ? F::fits_post : F::fits)
+    hipLaunchKernelGGL((pre_resident_kernel<NS, CPS, POST>), dim3(grid), dim3(kThreads), F::lds_bytes, s, a);
 }
 
 // Calls f.template operator()<NS, CPS>() for the runtime (n, cps).
@@ -502,24 +573,25 @@ auto dispatch(int n, int cps, Fn&& f) {
 #undef MHC_CPS
 }
 
+template <bool POST>
 struct OccQuery {
   template <int NS, int CPS>
-  int operator()() const { return occupancy_of<NS, CPS>(); }
+  int operator()() const { return occupancy_of<NS, CPS, POST>(); }
 };
 
-// Workgroups per CU for (n, cps) on the current device, cached; -1 when no
-// device answers (then a static estimate is used).
-int occupancy(int n, int cps) {
+// Workgroups per CU for (n, cps, layer boundary or not) on the current
+// device, cached; -1 when no device answers (then a static estimate is used).
+int occupancy(int n, int cps, bool post) {
   constexpr int kMaxDev = 64;
-  static std::atomic<int> cache[kMaxDev][5][16];
+  static std::atomic<int> cache[kMaxDev][2][5][16];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
   if (dev < kMaxDev) {
-    const int c = cache[dev][n][cps].load(std::memory_order_acquire);
+    const int c = cache[dev][post][n][cps].load(std::memory_order_acquire);
     if (c != 0) return c - 2;
   }
-  const int occ = dispatch(n, cps, OccQuery{});
-  if (dev < kMaxDev) cache[dev][n][cps].store(occ + 2, std::memory_order_release);
+  const int occ = post ? dispatch(n, cps, OccQuery<true>{}) : dispatch(n, cps, OccQuery<false>{});
+  if (dev < kMaxDev) cache[dev][post][n][cps].store(occ + 2, std::memory_order_release);
   return occ;
 }
 
@@ -532,7 +604,7 @@ int device_cus() {
 
 }  // namespace
 
-bool resident_choose(int64_t T, int n, int64_t D, mhc_dtype dt, ResidentChoice* out) {
+bool resident_choose(int64_t T, int n, int64_t D, mhc_dtype dt, ResidentChoice* out, bool post) {
   if (dt != MHC_BF16 || T <= 0 || n < 1 || n > 4 || D % 32 != 0) return false;
   const int tiles = (int)((T + kTM - 1) / kTM);
   const int cus = device_cus();
@@ -540,12 +612,13 @@ bool resident_choose(int64_t T, int n, int64_t D, mhc_dtype dt, ResidentChoice* 
   ResidentChoice best{};
   int best_launches = 0;
   for (int cps : kCpsList) {
-    if (D % (32 * cps) != 0 || 4 * n * cps > kMaxAVgprs) continue;
+    const int regs = 4 * n * cps + (post ? 4 * cps : 0);   // residual (+ block output) registers
+    if (D % (32 * cps) != 0 || regs > (post ? kMaxAVgprsPost : kMaxAVgprs)) continue;
     const int64_t S = D / (32 * cps);
     if (S > kMaxSplits) continue;
     if ((double)S * (double)T * (n * (n + 2) + 1) * 8.0 >= 2147483648.0) continue;   // 32-bit exchange offsets
-    int occ = occupancy(n, cps);
-    if (occ < 0) occ = 4 * n * cps > 96 ? 1 : 2;   // no device: static estimate
+    int occ = occupancy(n, cps, post);
+    if (occ < 0) occ = regs > 96 ? 1 : 2;   // no device: static estimate
     const int64_t cap = (int64_t)occ * cus;
     if (cap < S) continue;
     int per = (int)(cap / S);
@@ -574,23 +647,22 @@ bool resident_choose(int64_t T, int n, int64_t D, mhc_dtype dt, ResidentChoice* 
 }
 
 namespace {
+template <bool POST>
 struct Launcher {
   const ResArgs* a;
   unsigned grid;
   hipStream_t s;
   template <int NS, int CPS>
   int operator()() const {
-    launch_one<NS, CPS>(*a, grid, s);
+    launch_one<NS, CPS, POST>(*a, grid, s);
     return 0;
   }
 };
-}  // namespace
 
-hipError_t launch_pre_resident(const PrePlan& p, const void* residual, const float* fn, const float* hc_scale,
-                               const float* bias, float* post, float* comb, void* y, void* workspace, int repeat,
-                               float eps, hipStream_t s) {
+ResArgs resident_args(const PrePlan& p, const void* residual, const float* fn, const float* hc_scale,
+                      const float* bias, float* post, float* comb, void* y, void* workspace, int repeat, float eps) {
   char* ws = static_cast<char*>(workspace);
-  ResArgs a;
+  ResArgs a{};
   a.x = static_cast<const uint16_t*>(residual);
   a.fn = fn;
   a.hc_scale = hc_scale;
@@ -613,7 +685,28 @@ hipError_t launch_pre_resident(const PrePlan& p, const void* residual, const flo
   a.repeat = repeat;
   a.eps = eps;
   a.K = (float)p.K;
-  dispatch(p.n, p.rcps, Launcher{&a, (unsigned)a.P, s});
+  return a;
+}
+}  // namespace
+
+hipError_t launch_pre_resident(const PrePlan& p, const void* residual, const float* fn, const float* hc_scale,
+                               const float* bias, float* post, float* comb, void* y, void* workspace, int repeat,
+                               float eps, hipStream_t s) {
+  const ResArgs a = resident_args(p, residual, fn, hc_scale, bias, post, comb, y, workspace, repeat, eps);
+  dispatch(p.n, p.rcps, Launcher<false>{&a, (unsigned)a.P, s});
+  return hipGetLastError();
+}
+
+hipError_t launch_post_pre_resident(const PrePlan& p, const void* h, const void* residual, const float* post_in,
+                                    const float* comb_in, void* out, const float* fn, const float* hc_scale,
+                                    const float* bias, float* post, float* comb, void* y, void* workspace,
+                                    int repeat, float eps, hipStream_t s) {
+  ResArgs a = resident_args(p, residual, fn, hc_scale, bias, post, comb, y, workspace, repeat, eps);
+  a.h = static_cast<const uint16_t*>(h);
+  a.post_in = post_in;
+  a.comb_in = comb_in;
+  a.out = static_cast<uint16_t*>(out);
+  dispatch(p.n, p.rcps, Launcher<true>{&a, (unsigned)a.P, s});
   return hipGetLastError();
 }
 

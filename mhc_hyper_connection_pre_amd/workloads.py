@@ -39,8 +39,8 @@ from typing import Optional
 import numpy as np
 
 # stream ids spawned from the workload seed
-_S_RESIDUAL, _S_FN, _S_BIAS, _S_H, _S_OUTLIER, _S_COMBINE_W, _S_NORM_W = range(7)
-_N_STREAMS = 7
+_S_RESIDUAL, _S_FN, _S_BIAS, _S_H, _S_OUTLIER, _S_COMBINE_W, _S_NORM_W, _S_NEXT_FN = range(8)
+_N_STREAMS = 8
 _CHUNK_TOKENS = 256
 
 
@@ -164,3 +164,9 @@ def generate(s: Spec) -> Inputs:
         combine_w = rngs[_S_COMBINE_W].random((s.T, s.n), dtype=np.float32)
         norm_weight = (np.float32(0.5) + rngs[_S_NORM_W].random((s.D,), dtype=np.float32)).astype(np.float32)
     return Inputs(s, residual, fn, hc_scale, bias, h, combine_w, norm_weight)
+
+
+def next_layer_fn(s: Spec) -> np.ndarray:
+    """fn of the next layer for the layer-boundary call: the same distribution as ``fn``, its own stream."""
+    rng = np.random.default_rng(np.random.SeedSequence(s.seed).spawn(_N_STREAMS)[_S_NEXT_FN])
+    return (rng.standard_normal((s.K, s.N), dtype=np.float32) * np.float32(s.fn_std)).astype(np.float32)

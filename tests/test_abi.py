@@ -32,8 +32,8 @@ def L():
 
 def test_header_declares_the_boundary():
     syms = set(declared_symbols())
-    assert {"mhc_pre", "mhc_post", "mhc_post_combine_norm", "mhc_pre_workspace_bytes",
-            "mhc_pre_splits", "mhc_status_string", "mhc_last_error"} <= syms
+    assert {"mhc_pre", "mhc_post", "mhc_post_combine_norm", "mhc_post_pre", "mhc_pre_workspace_bytes",
+            "mhc_pre_splits", "mhc_post_pre_fused", "mhc_status_string", "mhc_last_error"} <= syms
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -129,6 +129,37 @@ def test_post_validation(L):
     assert post(out=None) == INVALID
     assert post(h=A + 4) == MISALIGNED
     assert post(c=A + 1) == MISALIGNED
+
+
+def test_post_pre_validation(L):
+    B = 0x100000
+    def pp(T=4, n=4, D=64, dt=BF16, out=B, pn=B + 0x10000, cn=B + 0x20000, y=B + 0x30000, h=B + 0x40000,
+           res=B + 0x50000, p=B + 0x60000, c=B + 0x70000, fn=B + 0x80000, hc=B + 0x90000, bias=B + 0xA0000,
+           R=20, eps=1e-6, sp=0, ws=None, wsb=0):
+        return L.mhc_post_pre(out, pn, cn, y, h, res, p, c, dt, fn, hc, bias, T, n, D, R, eps, sp, ws, wsb, None)
+    assert pp(T=0) == OK
+    assert pp(T=-1) == INVALID
+    assert pp(n=5) == UNSUPPORTED
+    assert pp(D=12) == MISALIGNED
+    assert pp(R=0) == INVALID
+    assert pp(eps=0.0) == INVALID
+    assert pp(sp=-2) == INVALID
+    assert pp(dt=F32, sp=-1) == UNSUPPORTED      # the single-pass kernel is bf16 only
+    assert pp(h=None) == INVALID
+    assert pp(fn=None) == INVALID
+    assert pp(out=B + 0x50000) == INVALID        # out over the residual
+    assert pp(out=B + 0x40000 - 64) == INVALID   # out over h
+    assert pp(y=B + 0x30008) == MISALIGNED
+    assert pp(c=B + 0x70001) == MISALIGNED
+    assert pp() == WORKSPACE                     # no workspace
+    need = L.mhc_pre_workspace_bytes(4, 4, 64, 0, BF16)
+    assert need > 0
+    assert pp(ws=B + 0x200000 + 8, wsb=need) == WORKSPACE   # not 256-byte aligned
+    assert pp(ws=B + 0x200000, wsb=need - 1) == WORKSPACE
+    assert L.mhc_post_pre_fused(2048, 4, 7168, 0, BF16) in (0, 1)
+    assert L.mhc_post_pre_fused(8, 4, 256, 0, F32) == 0
+    assert L.mhc_post_pre_fused(8, 4, 256, 3, BF16) == 0
+    assert L.mhc_post_pre_fused(8, 5, 256, 0, BF16) == UNSUPPORTED
 
 
 def test_post_combine_norm_validation(L):

@@ -1,0 +1,212 @@
+"""The layer boundary mhc_post_pre (post of the finished layer, then the next layer's pre) on the GPU.
+
+Compared with the float64 oracle's composition on the same seeded inputs, and
+with the two separate GPU calls. post and comb of the finished layer come from
+the oracle's pre on the same residual, so comb is a genuine Sinkhorn output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import mhc_hyper_connection_pre_amd as mhc
+from mhc_hyper_connection_pre_amd import workloads as W
+import oracle.mhc_oracle as O
+from parity import TOL_BF16, assert_close, decode, dev_tensor, host, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _case(x):
+    """Device inputs, plus the finished layer's post and comb (oracle pre of the residual with fn)."""
+    s = x.spec
+    post, comb, _ = O.mhc_pre(x.residual, x.fn, x.hc_scale, x.bias, n=s.n, D=s.D, dtype=s.dtype,
+                              sinkhorn_repeat=s.sinkhorn_repeat, eps=s.eps)
+    g = {k: dev_tensor(v) for k, v in x.arrays().items()}
+    g["post_in"], g["comb_in"] = dev_tensor(post), dev_tensor(comb)
+    fn2 = W.next_layer_fn(s)   # the next layer's fn
+    g["fn2"] = dev_tensor(fn2)
+    return g, post, comb, fn2
+
+
+def _workspace(s, n_splits):
+    need = mhc.mhc_pre_workspace_bytes(s.T, s.n, s.D, n_splits, 0 if s.dtype == "bf16" else 1)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    ws[:256].zero_()
+    return ws
+
+
+def _boundary(x, g, n_splits, ws):
+    s = x.spec
+    return mhc.mhc_post_pre(g["h"], g["residual"], g["post_in"], g["comb_in"], g["fn2"], g["hc_scale"], g["bias"],
+                            sinkhorn_repeat=s.sinkhorn_repeat, eps=s.eps, n_splits=n_splits, workspace=ws)
+
+
+def _ulp_bf16(v):
+    """Spacing of bf16 at |v| (one step up at the top of a binade, so a neighbour above is covered)."""
+    a = np.maximum(np.abs(v) * (1.0 + 2.0 ** -7), np.finfo(np.float32).tiny)
+    _, e = np.frexp(a)
+    return np.ldexp(1.0, e - 8)
+
+
+def _check_oracle(x, outs, post, comb, fn2, what):
+    """The oracle's composition (post, storage rounding, then pre on the stored out).
+
+    out: the GPU forms post_j h + sum_i comb_ij x_i as an fp32 chain (one
+    multiply, n FMAs) rounded once to bf16, the oracle in float64 rounded once,
+    so they may differ by one rounding decision (one bf16 ulp) plus the fp32
+    chain's error, at most (n + 1) 2^-24 (|post_j h| + sum_i |comb_ij x_i|); out
+    is checked against that bound. y' = sum_i pre_i out_i inherits up to
+    sum_i pre_i times that allowance, which cancellation in y' can make large
+    against y' itself; the propagated bound (from the oracle's own pre and the
+    inputs) is allowed on top of the usual tolerance. post' and comb' move by
+    far less than their tolerance.
+    """
+    s = x.spec
+    o_out, o_p, o_c, o_y = O.mhc_post_pre(x.h, x.residual, post, comb, fn2, x.hc_scale, x.bias, n=s.n, D=s.D,
+                                          dtype=s.dtype, sinkhorn_repeat=s.sinkhorn_repeat, eps=s.eps)
+    out, p, c, y = (host(t) for t in outs)
+    e1 = assert_close(p, o_p, "gate", f"{what} post'")
+    e2 = assert_close(c, o_c, "gate", f"{what} comb'")
+    if s.dtype != "bf16":
+        e0 = assert_close(out, o_out, "tensor", f"{what} out")
+        e3 = assert_close(y, o_y, "tensor", f"{what} y'")
+        _say(f"  {what}: out {e0:.2e} post' {e1:.2e} comb' {e2:.2e} y' {e3:.2e}")
+        return
+    g_out, w_out = decode(out), decode(o_out)
+    mag = (np.abs(post.astype(np.float64))[:, :, None] * np.abs(decode(x.h))[:, None, :]
+           + np.einsum("tij,tid->tjd", np.abs(comb.astype(np.float64)), np.abs(decode(x.residual))))
+    allow = _ulp_bf16(w_out) + (s.n + 1) * 2.0 ** -24 * mag
+    over = np.abs(g_out - w_out) / allow
+    assert np.max(over) <= 1.0, f"{what} out: {np.max(over):.2f} x the fp32-chain + rounding bound"
+    ulps = np.abs(g_out - w_out) / _ulp_bf16(w_out)
+    pre = O.mhc_pre(o_out, fn2, x.hc_scale, x.bias, n=s.n, D=s.D, dtype=s.dtype, sinkhorn_repeat=s.sinkhorn_repeat,
+                    eps=s.eps, intermediates=True)[3]["pre"]
+    bound = np.einsum("ti,tid->td", pre, allow)
+    g_y, w_y = decode(y), decode(o_y)
+    floor = 1e-3 * float(np.sqrt(np.mean(w_y * w_y)))
+    rel = np.maximum(np.abs(g_y - w_y) - bound, 0.0) / np.maximum(np.abs(w_y), floor)
+    e3 = float(np.max(rel)) if rel.size else 0.0
+    assert e3 <= TOL_BF16, f"{what} y': max rel err {e3:.3e} beyond the propagated out rounding"
+    _say(f"  {what}: out {np.count_nonzero(ulps)} of {ulps.size} off (max {np.max(ulps):.1f} ulp); post' {e1:.2e} comb' {e2:.2e} "
+         f"y' {e3:.2e} (plain {rel_err(y, o_y, 'tensor'):.2e})")
+
+
+FUSED = [(1, 4, 512), (31, 4, 1024), (67, 3, 1024), (130, 2, 512), (17, 1, 2048), (64, 4, 5120),
+         (129, 4, 1056), (300, 3, 2240), (1100, 4, 7168)]   # the last: two generations, the second ragged
+FALLBACK = [(7, 4, 264, "bf16"), (33, 4, 1032, "f32"), (5, 2, 72, "bf16")]
+
+
+@pytest.mark.parametrize("T,n,D", FUSED, ids=lambda v: str(v))
+def test_boundary_fused(T, n, D):
+    assert mhc.mhc_post_pre_fused(T, n, D, 0, 0)
+    x = W.generate(W.custom(T, n, D, "bf16", seed=T * 5 + n * 3 + D, fn_std=0.02))
+    g, post, comb, fn2 = _case(x)
+    ws = _workspace(x.spec, 0)
+    outs = _boundary(x, g, 0, ws)
+    assert mhc.mhc_pre_sync_timeouts(ws, g["residual"], 0) == 0
+    torch.cuda.synchronize()
+    _check_oracle(x, outs, post, comb, fn2, f"fused T{T} n{n} D{D}")
+    # the two separate calls: out bit for bit, the pre outputs to the path's rounding
+    sep_out = mhc.mhc_post(g["h"], g["residual"], g["post_in"], g["comb_in"])
+    sp, sc, sy = mhc.mhc_pre(sep_out, g["fn2"], g["hc_scale"], g["bias"], sinkhorn_repeat=x.spec.sinkhorn_repeat,
+                             eps=x.spec.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], sep_out), "boundary out differs from mhc_post"
+    for u, v, k in zip(outs[1:], (sp, sc, sy), ("post", "comb", "y")):
+        u = u.float().cpu().numpy().astype(np.float64)
+        v = v.float().cpu().numpy().astype(np.float64)
+        d = np.max(np.abs(u - v) / np.maximum(np.abs(v), 1e-3 if k == "y" else 1e-6))
+        assert d <= (1e-2 if k == "y" else 1e-4), (k, d)
+
+
+@pytest.mark.parametrize("T,n,D,dt", FALLBACK, ids=lambda v: str(v))
+def test_boundary_fallback(T, n, D, dt):
+    """Shapes the single-pass kernel does not cover run mhc_post's and mhc_pre's kernels in sequence."""
+    assert not mhc.mhc_post_pre_fused(T, n, D, 0, 0 if dt == "bf16" else 1)
+    x = W.generate(W.custom(T, n, D, dt, seed=T + n + D, fn_std=0.05))
+    g, post, comb, fn2 = _case(x)
+    outs = _boundary(x, g, 0, _workspace(x.spec, 0))
+    torch.cuda.synchronize()
+    _check_oracle(x, outs, post, comb, fn2, f"fallback T{T} n{n} D{D} {dt}")
+
+
+def test_boundary_explicit_splits_two_pass():
+    x = W.generate(W.custom(70, 4, 1024, "bf16", seed=123, fn_std=0.02))
+    g, post, comb, fn2 = _case(x)
+    assert not mhc.mhc_post_pre_fused(70, 4, 1024, 3, 0)
+    outs = _boundary(x, g, 3, _workspace(x.spec, 3))
+    torch.cuda.synchronize()
+    _check_oracle(x, outs, post, comb, fn2, "n_splits 3")
+
+
+def test_boundary_metric_workload():
+    """T = 2048, n = 4, D = 7168 in full, in the launch configuration bench.py times."""
+    x = W.generate(W.spec("prefill-d7168"))
+    g, post, comb, fn2 = _case(x)
+    ws = _workspace(x.spec, 0)
+    outs = _boundary(x, g, 0, ws)
+    assert mhc.mhc_pre_sync_timeouts(ws, g["residual"], 0) == 0
+    torch.cuda.synchronize()
+    _check_oracle(x, outs, post, comb, fn2, "prefill-d7168")
+
+
+def test_boundary_shares_workspace_with_pre():
+    """mhc_pre and mhc_post_pre alternate on one workspace (epochs and tag regions carry over)."""
+    x = W.generate(W.custom(300, 4, 2048, "bf16", seed=55, fn_std=0.02))
+    g, post, comb, fn2 = _case(x)
+    s = x.spec
+    ws = _workspace(s, 0)
+    want_pre = O.mhc_pre(x.residual, x.fn, x.hc_scale, x.bias, n=s.n, D=s.D, dtype=s.dtype,
+                         sinkhorn_repeat=s.sinkhorn_repeat, eps=s.eps)
+    for k in range(3):
+        outs = _boundary(x, g, 0, ws)
+        p, c, y = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], sinkhorn_repeat=s.sinkhorn_repeat,
+                              eps=s.eps, workspace=ws)
+        torch.cuda.synchronize()
+        _check_oracle(x, outs, post, comb, fn2, f"boundary round {k}")
+        for got, want, kind, name in zip((p, c, y), want_pre, ("gate", "gate", "tensor"), ("post", "comb", "y")):
+            assert_close(host(got), want, kind, f"pre round {k} {name}")
+
+
+def test_boundary_graph_replay():
+    """Captured once, replayed three times with eager calls on the same workspace in between."""
+    x = W.generate(W.custom(257, 4, 1024, "bf16", seed=66, fn_std=0.02))
+    g, post, comb, fn2 = _case(x)
+    s = x.spec
+    ws = _workspace(s, 0)
+    eager = [t.clone() for t in _boundary(x, g, 0, ws)]
+    bufs = [torch.empty_like(t) for t in eager]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mhc.mhc_post_pre(g["h"], g["residual"], g["post_in"], g["comb_in"], g["fn2"], g["hc_scale"], g["bias"],
+                         sinkhorn_repeat=s.sinkhorn_repeat, eps=s.eps, out=bufs[0], post_next=bufs[1],
+                         comb_next=bufs[2], y=bufs[3], workspace=ws, stream=torch.cuda.current_stream())
+    for k in range(3):
+        for b in bufs:
+            b.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for b, e in zip(bufs, eager):
+            assert torch.equal(b, e), f"replay {k} differs from the eager call"
+        _boundary(x, g, 0, ws)   # an eager call between replays
+        torch.cuda.synchronize()
+
+
+def test_boundary_errors():
+    x = W.generate(W.custom(8, 4, 512, "bf16", seed=7))
+    g, _, _, _ = _case(x)
+    with pytest.raises(mhc.MhcError) as e:   # out over the residual
+        mhc.mhc_post_pre(g["h"], g["residual"], g["post_in"], g["comb_in"], g["fn2"], g["hc_scale"], g["bias"],
+                         out=g["residual"])
+    assert e.value.status == -1
+    r32 = g["residual"].float()
+    with pytest.raises(mhc.MhcError) as e:   # single-pass asked for an fp32 residual
+        mhc.mhc_post_pre(g["h"].float(), r32, g["post_in"], g["comb_in"], g["fn2"], g["hc_scale"], g["bias"],
+                         n_splits=-1)
+    assert e.value.status == -2
