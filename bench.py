@@ -9,11 +9,18 @@ resident in HBM when the timed region starts. Steps rotate over several input
 and output buffer sets so that no step reads data the previous step left in
 the 256 MB Infinity Cache.
 
+Timing: the K timed steps run with nothing between the launches (value,
+ms_per_step); the same K steps then run again with a HIP event on the launch
+stream around every call (events without the system-scope fence), which gives
+each kernel's average duration. For the prefill workloads a third pass times
+the layer boundary as one call, mhc_post_pre (post of one layer, then the next
+layer's pre), on the same buffers ("boundary").
+
 Prints one JSON line: tokens/s (value), algorithmic HBM GB/s and its fraction
 of the 8 TB/s peak, a roofline object for the dominant kernel (algorithmic
-bytes per launch / average launch duration from HIP events recorded on the
-launch stream; the pre call, with the post call beside it as roofline_tail),
-and the CPU oracle timed on the host as a baseline.
+bytes per launch / average launch duration from the events; the pre call,
+with the post call beside it as roofline_tail), the boundary call, and the
+CPU oracle timed on the host as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        python bench.py --summarize-rocprof DIR   (summarise rocprofv3 output)
@@ -60,6 +67,14 @@ def pre_bytes(T, n, D, e):
 def post_bytes(T, n, D, e):
     """h, residual, post + comb read once; out written once."""
     return T * D * e + T * n * D * e + T * (n + n * n) * 4 + T * n * D * e
+
+
+def boundary_bytes(T, n, D, e):
+    """mhc_post_pre: h, residual, post, comb, the next layer's fn, hc_scale and bias read once; out, y, post
+    and comb of the next layer written once (out is never read back)."""
+    N = n * (n + 2)
+    return (T * D * e + T * n * D * e + T * (n + n * n) * 4 + n * D * N * 4 + (N + 3) * 4
+            + T * n * D * e + T * D * e + T * (n + n * n) * 4)
 
 
 def pcn_bytes(T, n, D, e):
@@ -160,6 +175,43 @@ def summarize_rocprof(d):
             rows.setdefault(k, {})[c + "_n"] = len(v)
     for k, v in sorted(rows.items(), key=lambda kv: -kv[1].get("total_us", 0)):
         print(json.dumps({"kernel": k, **v}))
+
+
+# ---------------------------------------------------------------- timing events
+
+class HipEvents:
+    """HIP events without the system-scope fence, recorded on a given stream (per-kernel durations)."""
+
+    def __init__(self, stream_handle, count):
+        import ctypes
+        self._c = ctypes
+        self._hip = ctypes.CDLL("libamdhip64.so")   # the HIP runtime torch has loaded
+        self._hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self._hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._stream = ctypes.c_void_p(stream_handle)
+        self._ev = []
+        for _ in range(count):
+            e = ctypes.c_void_p()
+            if self._hip.hipEventCreateWithFlags(ctypes.byref(e), 0x20000000) != 0:   # hipEventDisableSystemFence
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self._ev.append(e)
+
+    def record(self, i):
+        if self._hip.hipEventRecord(self._ev[i], self._stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, i, j):
+        f = self._c.c_float()
+        if self._hip.hipEventElapsedTime(self._c.byref(f), self._ev[i], self._ev[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return f.value
+
+    def destroy(self):
+        for e in self._ev:
+            self._hip.hipEventDestroy(e)
+        self._ev = []
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -296,21 +348,66 @@ def run(args):
         def run_post(k):
             graphs[k][1].replay()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # The timed steps: nothing but the calls between the two synchronisations
+    # (an event record between kernels costs the next kernel several us here).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        ev = events[i]
-        ev[0].record(stream)
         run_pre(i % nsets)
-        ev[1].record(stream)
         run_post(i % nsets)
-        ev[2].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    pre_ms = sum(ev[0].elapsed_time(ev[1]) for ev in events) / args.steps
-    post_ms = sum(ev[1].elapsed_time(ev[2]) for ev in events) / args.steps
+
+    # The same steps again with a HIP event on the launch stream around every
+    # call, for the per-kernel durations. The events skip the system-scope
+    # fence (hipEventDisableSystemFence): a default event writes back and
+    # invalidates the caches, which slows the kernel after it.
+    ev = HipEvents(stream.cuda_stream, 3 * args.steps)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(args.steps):
+        ev.record(3 * i)
+        run_pre(i % nsets)
+        ev.record(3 * i + 1)
+        run_post(i % nsets)
+        ev.record(3 * i + 2)
+    torch.cuda.synchronize()
+    ms_per_step_events = (time.perf_counter() - t2) * 1e3 / args.steps
+    pre_ms = sum(ev.elapsed_ms(3 * i, 3 * i + 1) for i in range(args.steps)) / args.steps
+    post_ms = sum(ev.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(args.steps)) / args.steps
+    ev.destroy()
+
+    # The layer boundary (mhc_post of one layer, then the next layer's mhc_pre)
+    # as one call, on the same buffer sets: the post and comb each set's pre
+    # wrote stand for the finished layer's, fn for the next layer's.
+    boundary = None
+    if not fused_tail:
+        for b in sets:
+            b["post_next"] = torch.empty_like(b["post"])
+            b["comb_next"] = torch.empty_like(b["comb"])
+
+        def run_boundary(k):
+            b = sets[k]
+            mhc.mhc_post_pre(b["h"], b["residual"], b["post"], b["comb"], fn, hc, bias,
+                             sinkhorn_repeat=spec.sinkhorn_repeat, eps=spec.eps, n_splits=spec.n_splits,
+                             out=b["out"], post_next=b["post_next"], comb_next=b["comb_next"], y=b["y"],
+                             workspace=ws, stream=stream)
+
+        for i in range(args.warmup):
+            run_boundary(i % nsets)
+        torch.cuda.synchronize()
+        t3 = time.perf_counter()
+        for i in range(args.steps):
+            run_boundary(i % nsets)
+        torch.cuda.synchronize()
+        us_b = (time.perf_counter() - t3) * 1e6 / args.steps
+        bb = boundary_bytes(T, n, D, e)
+        boundary = {"call": "mhc_post_pre", "one_launch": bool(mhc.mhc_post_pre_fused(T, n, D, spec.n_splits,
+                                                                                      0 if spec.dtype == "bf16" else 1)),
+                    "us_per_call": us_b, "tokens_per_s": T / (us_b * 1e-6), "algorithmic_bytes": bb,
+                    "gbps": bb / (us_b * 1e-6) / 1e9, "frac_of_peak": bb / (us_b * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                    "vs_pre_plus_post_step": ms_per_step * 1e3 / us_b}
 
     # practical ceiling: a 1 GiB device-to-device copy kernel on the same stream
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -354,6 +451,7 @@ def run(args):
         "hbm_gbps": step_gbps,
         "hbm_frac_of_peak": step_gbps / PEAK_HBM_GBPS,
         "algorithmic_bytes_per_step": bp + bq,
+        "ms_per_step_with_events": ms_per_step_events,
         "pre_us": pre_ms * 1e3,
         "post_us": post_ms * 1e3,
         "pre_gbps": pre_gbps,
@@ -361,6 +459,7 @@ def run(args):
         "copy_gbps_1GiB": copy_gbps,
         "hbm_frac_of_copy": step_gbps / copy_gbps,
         "tail": "mhc_post_combine_norm (fused, writes out too)" if fused_tail else "mhc_post",
+        "boundary": boundary,
         # the pre call is the longer of the two
         "roofline": {"kernel": pre_kernel, "bound": "hbm", "achieved": pre_gbps,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": pre_gbps / PEAK_HBM_GBPS,

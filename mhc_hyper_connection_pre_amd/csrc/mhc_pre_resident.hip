@@ -196,34 +196,43 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
   // or stored), issued column by column (k-step c of every stream, then the
   // block output's column c at the layer boundary), the order in which y
   // frees the registers and the GEMM consumes them.
+  // Addresses: a uniform base per tile (and per stream) plus one 32-bit lane
+  // offset, so the loads and stores take the base from scalar registers and
+  // the column offset as an immediate (the lane offsets stay below 2^31: the
+  // host bounds kTM * n * D). lane_row: this lane's row in tile t, or row 0
+  // of the tile past T (read, never published or stored).
+  auto lane_row = [&](int t) { return (int64_t)t * kTM + w * 16 + r16 < T ? w * 16 + r16 : 0; };
+  auto load_col = [&](int t, int lr, int c) {
+    const uint16_t* xb = a.x + (int64_t)t * kTM * NS * D + d0;
+    const uint32_t xo = (uint32_t)(lr * NS * (int)D + q * 8);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      A[i * CPS + c] = ld16(xb + i * D + xo + c * 32);
+      __builtin_amdgcn_sched_barrier(0);   // issue in exactly this order (the waits depend on it)
+    }
+    if constexpr (POST) {
+      const uint16_t* hb = a.h + (int64_t)t * kTM * D + d0;
+      H[c] = ld16(hb + (uint32_t)(lr * (int)D + q * 8) + c * 32);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   auto load_cols = [&](int t, auto c0_tag, auto c1_tag) {
     constexpr int C0 = decltype(c0_tag)::value, C1 = decltype(c1_tag)::value;
-    const int64_t rw0 = (int64_t)t * kTM + w * 16 + r16;
-    const int64_t rr = rw0 < T ? rw0 : 0;
-    const uint16_t* xr = a.x + rr * NS * D + d0 + q * 8;
+    const int lr = lane_row(t);
 #pragma unroll
-    for (int c = C0; c < C1; ++c) {
-#pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        A[i * CPS + c] = ld16(xr + i * D + c * 32);
-        __builtin_amdgcn_sched_barrier(0);   // issue in exactly this order (the waits depend on it)
-      }
-      if constexpr (POST) {
-        H[c] = ld16(a.h + rr * D + d0 + q * 8 + c * 32);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+    for (int c = C0; c < C1; ++c) load_col(t, lr, c);
   };
   // layer boundary: post and comb of the finished layer for this lane's token
   // of tile t, issued ahead of the tile's residual
   auto load_pw = [&](int t) {
     if constexpr (POST) {
-      const int64_t rw0 = (int64_t)t * kTM + w * 16 + r16;
-      const int64_t rr = rw0 < T ? rw0 : 0;
+      const int lr = lane_row(t);
+      const float* pb = a.post_in + (int64_t)t * kTM * NS;
+      const float* cb = a.comb_in + (int64_t)t * kTM * NS * NS;
 #pragma unroll
-      for (int j = 0; j < NS; ++j) pw[j] = a.post_in[rr * NS + j];
+      for (int j = 0; j < NS; ++j) pw[j] = pb[lr * NS + j];
 #pragma unroll
-      for (int k = 0; k < NS * NS; ++k) pw[NS + k] = a.comb_in[rr * NS * NS + k];
+      for (int k = 0; k < NS * NS; ++k) pw[NS + k] = cb[lr * NS * NS + k];
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -297,11 +306,19 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
   // residual is loaded into the registers that y frees
   auto generation = [&](auto next_tag) {
     constexpr bool NEXT = decltype(next_tag)::value;
-    // this tile's residual slice is in flight (rows past T read row 0 and are
-    // never published or stored): issued before the packing for the first
-    // generation, during the previous generation's y otherwise
+    // this tile's residual slice is in flight (rows past T read the tile's
+    // first row and are never published or stored): issued before the packing
+    // for the first generation, during the previous generation's y otherwise
     const int64_t row = (int64_t)tile * kTM + w * 16 + r16;
     const bool rok = row < T;
+
+    // layer boundary: where this lane's out values go
+    uint16_t* ob = nullptr;
+    uint32_t oo = 0;
+    if constexpr (POST) {
+      ob = a.out + (int64_t)tile * kTM * NS * D + d0;
+      oo = (uint32_t)((w * 16 + r16) * NS * (int)D + q * 8);
+    }
 
     // ---- 1. split-K GEMM + sum of squares, each k-step as its residual arrives
     f32x4 acc[NCB];
@@ -313,7 +330,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
       if constexpr (POST) {
         // column c of the new residual, out_j = post_j h + sum_i comb[i][j]
         // x_i, in fp32 with the operation order and the single rounding of
-        // mhc_post; stored, then the GEMM's A operand in place of x_j
+        // mhc_post: the GEMM's A operand in place of x_j (stored below)
         u32x4 ov[NS];
 #pragma unroll
         for (int wd = 0; wd < 4; ++wd) {
@@ -336,10 +353,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
           }
         }
 #pragma unroll
-        for (int jj = 0; jj < NS; ++jj) {
-          A[jj * CPS + c] = ov[jj];
-          if (rok) st16_stream(a.out + row * NS * D + jj * D + d0 + q * 8 + c * 32, ov[jj]);
-        }
+        for (int jj = 0; jj < NS; ++jj) A[jj * CPS + c] = ov[jj];
       }
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
@@ -379,6 +393,16 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
       }
     }
     __syncthreads();   // the scratch is reused below
+    // layer boundary: out goes to HBM now, while the tile's exchange below
+    // leaves HBM mostly idle (stored during the GEMM it competed with the
+    // residual loads: 8 us more per call at T = 2048, n = 4, D = 7168)
+    if constexpr (POST) {
+#pragma unroll
+      for (int c = 0; c < CPS; ++c)
+#pragma unroll
+        for (int jj = 0; jj < NS; ++jj)
+          if (rok) st16_stream(ob + jj * D + oo + c * 32, A[jj * CPS + c]);
+    }
     // ---- 3. finalise tokens sg, sg + S, ... of the tile, TB at a time. Thread
     // (c = tid % 32, group = tid / 32) sums column c of splits sub, sub + SUBS,
     // ... (sub = group % SUBS) of token group / SUBS of the batch; the SUBS sums
@@ -477,10 +501,9 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
     // y column by column; the registers of a column are refilled with the next
     // tile's residual right after, so those loads overlap the rest of y
     {
-      uint16_t* yr = a.y + row * D + d0 + q * 8;
-      const int64_t nrow = (int64_t)(tile + G) * kTM + w * 16 + r16;
-      const int64_t nrr = nrow < T ? nrow : 0;
-      const uint16_t* nxr = a.x + nrr * NS * D + d0 + q * 8;
+      uint16_t* yb = a.y + (int64_t)tile * kTM * D + d0;
+      const uint32_t yo = (uint32_t)((w * 16 + r16) * (int)D + q * 8);
+      const int nlr = lane_row(tile + G);
       if constexpr (NEXT) load_pw(tile + G);
 #pragma unroll
       for (int c = 0; c < CPS; ++c) {
@@ -494,18 +517,8 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
 #pragma unroll
           for (int v = 0; v < 8; ++v) o[v] = fmaf(pre[i], f[v], o[v]);
         }
-        if (rok) st16_stream(yr + c * 32, Vec<BF16>::pack(o));
-        if constexpr (NEXT) {
-#pragma unroll
-          for (int i = 0; i < NS; ++i) {
-            A[i * CPS + c] = ld16(nxr + i * D + c * 32);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-          if constexpr (POST) {
-            H[c] = ld16(a.h + nrr * D + d0 + q * 8 + c * 32);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
+        if (rok) st16_stream(yb + yo + c * 32, Vec<BF16>::pack(o));
+        if constexpr (NEXT) load_col(tile + G, nlr, c);
       }
     }
   };
@@ -606,6 +619,7 @@ int device_cus() {
 
 bool resident_choose(int64_t T, int n, int64_t D, mhc_dtype dt, ResidentChoice* out, bool post) {
   if (dt != MHC_BF16 || T <= 0 || n < 1 || n > 4 || D % 32 != 0) return false;
+  if ((int64_t)kTM * n * D >= (1LL << 31)) return false;   // 32-bit lane offsets within a tile
   const int tiles = (int)((T + kTM - 1) / kTM);
   const int cus = device_cus();
   bool found = false;
