@@ -48,10 +48,11 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "mhc_hyper_connection_pre_amd", "csrc")
 # Counter-derived HBM traffic per launch of the two kernels of the default
 # workload: the profile file and the sources its number holds for.
+_RESIDENT_SOURCES = ["mhc_pre_resident.hip", "mhc_device.h", "mhc_pack.h", "mhc_epilogue.h", "mhc_internal.h"]
 TRAFFIC = {
-    "pre": ("traffic_pre_resident_prefill-d7168.txt", "pre_resident_kernel",
-            ["mhc_pre_resident.hip", "mhc_device.h", "mhc_pack.h", "mhc_epilogue.h", "mhc_internal.h"]),
+    "pre": ("traffic_pre_resident_prefill-d7168.txt", "pre_resident_kernel<4, 7, false>", _RESIDENT_SOURCES),
     "post": ("traffic_post_prefill-d7168.txt", "post_kernel<", ["mhc_post.hip", "mhc_device.h"]),
+    "boundary": ("traffic_boundary_prefill-d7168.txt", "pre_resident_kernel<4, 7, true>", _RESIDENT_SOURCES),
 }
 COPY_KIB = 1 << 20   # the 1 GiB calibration copy bench.py runs, in KiB read and written
 
@@ -132,7 +133,7 @@ def write_traffic(fetch_dir, write_dir, command):
     fs = COPY_KIB / max(fetch[copy[0]])
     ws = COPY_KIB / max(write[copy[0]])
     T, n, D, e = 2048, 4, 7168, 2
-    algo = {"pre": pre_bytes(T, n, D, e), "post": post_bytes(T, n, D, e)}
+    algo = {"pre": pre_bytes(T, n, D, e), "post": post_bytes(T, n, D, e), "boundary": boundary_bytes(T, n, D, e)}
     for which, (fname, key, sources) in TRAFFIC.items():
         names = [k for k in fetch if key in k]
         if not names or names[0] not in write:
@@ -381,6 +382,7 @@ def run(args):
     # The layer boundary (mhc_post of one layer, then the next layer's mhc_pre)
     # as one call, on the same buffer sets: the post and comb each set's pre
     # wrote stand for the finished layer's, fn for the next layer's.
+    default_wl = args.workload == W.THROUGHPUT_WORKLOAD and spec.n_splits == W.spec(args.workload).n_splits
     boundary = None
     if not fused_tail:
         for b in sets:
@@ -403,8 +405,9 @@ def run(args):
         torch.cuda.synchronize()
         us_b = (time.perf_counter() - t3) * 1e6 / args.steps
         bb = boundary_bytes(T, n, D, e)
-        boundary = {"call": "mhc_post_pre", "one_launch": bool(mhc.mhc_post_pre_fused(T, n, D, spec.n_splits,
-                                                                                      0 if spec.dtype == "bf16" else 1)),
+        one = bool(mhc.mhc_post_pre_fused(T, n, D, spec.n_splits, 0 if spec.dtype == "bf16" else 1))
+        boundary = {"call": "mhc_post_pre", "one_launch": one,
+                    "traffic": stored_traffic("boundary") if default_wl and one else None,
                     "us_per_call": us_b, "tokens_per_s": T / (us_b * 1e-6), "algorithmic_bytes": bb,
                     "gbps": bb / (us_b * 1e-6) / 1e9, "frac_of_peak": bb / (us_b * 1e-6) / 1e9 / PEAK_HBM_GBPS,
                     "vs_pre_plus_post_step": ms_per_step * 1e3 / us_b}
@@ -427,7 +430,6 @@ def run(args):
     step_gbps = (bp + bq) / (ms_per_step * 1e-3) / 1e9
     post_gbps = bq / (post_ms * 1e-3) / 1e9
     pre_gbps = bp / (pre_ms * 1e-3) / 1e9
-    default_wl = args.workload == W.THROUGHPUT_WORKLOAD and spec.n_splits == W.spec(args.workload).n_splits
     pre_kernel = ("pre_resident_kernel (mhc_pre, one launch)" if single
                   else "mhc_pre (fn pack + split-K GEMM + epilogue launches)")
     tail_kernel = "post_combine_norm_kernel" if fused_tail else "post_kernel (mhc_post)"
