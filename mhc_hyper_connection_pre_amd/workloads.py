@@ -39,8 +39,8 @@ from typing import Optional
 import numpy as np
 
 # stream ids spawned from the workload seed
-_S_RESIDUAL, _S_FN, _S_BIAS, _S_H, _S_OUTLIER, _S_COMBINE_W, _S_NORM_W, _S_NEXT_FN = range(8)
-_N_STREAMS = 8
+_S_RESIDUAL, _S_FN, _S_BIAS, _S_H, _S_OUTLIER, _S_COMBINE_W, _S_NORM_W, _S_NEXT_FN, _S_MIX = range(9)
+_N_STREAMS = 9
 _CHUNK_TOKENS = 256
 
 
@@ -170,3 +170,12 @@ def next_layer_fn(s: Spec) -> np.ndarray:
     """fn of the next layer for the layer-boundary call: the same distribution as ``fn``, its own stream."""
     rng = np.random.default_rng(np.random.SeedSequence(s.seed).spawn(_N_STREAMS)[_S_NEXT_FN])
     return (rng.standard_normal((s.K, s.N), dtype=np.float32) * np.float32(s.fn_std)).astype(np.float32)
+
+
+def mixing_weights(s: Spec):
+    """post [T, n] ~ U(0, 1) and comb [T, n, n] ~ U(0, 1) / n (float32) for post-step tests at sizes where
+    computing them with a pre step on the host would be slow; drawn directly, not by the method."""
+    rng = np.random.default_rng(np.random.SeedSequence(s.seed).spawn(_N_STREAMS)[_S_MIX])
+    post = rng.random((s.T, s.n), dtype=np.float32)
+    comb = (rng.random((s.T, s.n, s.n), dtype=np.float32) / np.float32(s.n)).astype(np.float32)
+    return post, comb

@@ -53,7 +53,7 @@ def _ulp_bf16(v):
     return np.ldexp(1.0, e - 8)
 
 
-def _check_oracle(x, outs, post, comb, fn2, what):
+def _check_oracle(x, outs, post, comb, fn2, what, tokens=None):
     """The oracle's composition (post, storage rounding, then pre on the stored out).
 
     out: the GPU forms post_j h + sum_i comb_ij x_i as an fp32 chain (one
@@ -67,9 +67,13 @@ def _check_oracle(x, outs, post, comb, fn2, what):
     far less than their tolerance.
     """
     s = x.spec
-    o_out, o_p, o_c, o_y = O.mhc_post_pre(x.h, x.residual, post, comb, fn2, x.hc_scale, x.bias, n=s.n, D=s.D,
-                                          dtype=s.dtype, sinkhorn_repeat=s.sinkhorn_repeat, eps=s.eps)
+    h, res = x.h, x.residual
     out, p, c, y = (host(t) for t in outs)
+    if tokens is not None:   # tokens are independent: the oracle runs on the sampled ones only
+        h, res, post, comb = h[tokens], res[tokens], post[tokens], comb[tokens]
+        out, p, c, y = out[tokens], p[tokens], c[tokens], y[tokens]
+    o_out, o_p, o_c, o_y = O.mhc_post_pre(h, res, post, comb, fn2, x.hc_scale, x.bias, n=s.n, D=s.D,
+                                          dtype=s.dtype, sinkhorn_repeat=s.sinkhorn_repeat, eps=s.eps)
     e1 = assert_close(p, o_p, "gate", f"{what} post'")
     e2 = assert_close(c, o_c, "gate", f"{what} comb'")
     if s.dtype != "bf16":
@@ -78,8 +82,8 @@ def _check_oracle(x, outs, post, comb, fn2, what):
         _say(f"  {what}: out {e0:.2e} post' {e1:.2e} comb' {e2:.2e} y' {e3:.2e}")
         return
     g_out, w_out = decode(out), decode(o_out)
-    mag = (np.abs(post.astype(np.float64))[:, :, None] * np.abs(decode(x.h))[:, None, :]
-           + np.einsum("tij,tid->tjd", np.abs(comb.astype(np.float64)), np.abs(decode(x.residual))))
+    mag = (np.abs(post.astype(np.float64))[:, :, None] * np.abs(decode(h))[:, None, :]
+           + np.einsum("tij,tid->tjd", np.abs(comb.astype(np.float64)), np.abs(decode(res))))
     allow = _ulp_bf16(w_out) + (s.n + 1) * 2.0 ** -24 * mag
     over = np.abs(g_out - w_out) / allow
     assert np.max(over) <= 1.0, f"{what} out: {np.max(over):.2f} x the fp32-chain + rounding bound"
@@ -153,6 +157,29 @@ def test_boundary_metric_workload():
     assert mhc.mhc_pre_sync_timeouts(ws, g["residual"], 0) == 0
     torch.cuda.synchronize()
     _check_oracle(x, outs, post, comb, fn2, "prefill-d7168")
+
+
+@pytest.mark.slow
+def test_boundary_large_sampled():
+    """T = 16384 (sixteen generations), residual with 1 % outliers x50: compared on sampled tokens, with
+    the finished layer's post and comb drawn for every token by the workload generator."""
+    s = W.spec("prefill-t16384-d7168")
+    x = W.generate(s)
+    assert mhc.mhc_post_pre_fused(s.T, s.n, s.D, 0, 0)
+    post, comb = W.mixing_weights(s)
+    fn2 = W.next_layer_fn(s)
+    g = {k: dev_tensor(v) for k, v in x.arrays().items()}
+    g["post_in"], g["comb_in"], g["fn2"] = dev_tensor(post), dev_tensor(comb), dev_tensor(fn2)
+    ws = _workspace(s, 0)
+    outs = _boundary(x, g, 0, ws)
+    assert mhc.mhc_pre_sync_timeouts(ws, g["residual"], 0) == 0
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(98)
+    tokens = np.unique(np.concatenate([[0, 1, 2047, 2048, s.T - 1], rng.choice(s.T, 123, replace=False)]))
+    _check_oracle(x, outs, post, comb, fn2, "T16384 sampled", tokens=tokens)
+    c = host(outs[2]).astype(np.float64)   # properties of comb' at every token
+    assert np.all(c >= 0) and np.max(np.abs(c.sum(axis=1) - 1)) <= 1e-5
+    del g, outs
 
 
 def test_boundary_shares_workspace_with_pre():
