@@ -12,9 +12,9 @@ the 256 MB Infinity Cache.
 Timing: the K timed steps run with nothing between the launches (value,
 ms_per_step); the same K steps then run again with a HIP event on the launch
 stream around every call (events without the system-scope fence), which gives
-each kernel's average duration. For the prefill workloads a third pass times
-the layer boundary as one call, mhc_post_pre (post of one layer, then the next
-layer's pre), on the same buffers ("boundary").
+each kernel's average duration. A third pass times the layer boundary as one
+call, mhc_post_pre (post of one layer, then the next layer's pre), on the same
+buffers ("boundary").
 
 Prints one JSON line: tokens/s (value), algorithmic HBM GB/s and its fraction
 of the 8 TB/s peak, a roofline object for the dominant kernel (algorithmic
@@ -383,34 +383,32 @@ def run(args):
     # as one call, on the same buffer sets: the post and comb each set's pre
     # wrote stand for the finished layer's, fn for the next layer's.
     default_wl = args.workload == W.THROUGHPUT_WORKLOAD and spec.n_splits == W.spec(args.workload).n_splits
-    boundary = None
-    if not fused_tail:
-        for b in sets:
-            b["post_next"] = torch.empty_like(b["post"])
-            b["comb_next"] = torch.empty_like(b["comb"])
+    for b in sets:
+        b["post_next"] = torch.empty_like(b["post"])
+        b["comb_next"] = torch.empty_like(b["comb"])
 
-        def run_boundary(k):
-            b = sets[k]
-            mhc.mhc_post_pre(b["h"], b["residual"], b["post"], b["comb"], fn, hc, bias,
-                             sinkhorn_repeat=spec.sinkhorn_repeat, eps=spec.eps, n_splits=spec.n_splits,
-                             out=b["out"], post_next=b["post_next"], comb_next=b["comb_next"], y=b["y"],
-                             workspace=ws, stream=stream)
+    def run_boundary(k):
+        b = sets[k]
+        mhc.mhc_post_pre(b["h"], b["residual"], b["post"], b["comb"], fn, hc, bias,
+                         sinkhorn_repeat=spec.sinkhorn_repeat, eps=spec.eps, n_splits=spec.n_splits,
+                         out=b["out"], post_next=b["post_next"], comb_next=b["comb_next"], y=b["y"],
+                         workspace=ws, stream=stream)
 
-        for i in range(args.warmup):
-            run_boundary(i % nsets)
-        torch.cuda.synchronize()
-        t3 = time.perf_counter()
-        for i in range(args.steps):
-            run_boundary(i % nsets)
-        torch.cuda.synchronize()
-        us_b = (time.perf_counter() - t3) * 1e6 / args.steps
-        bb = boundary_bytes(T, n, D, e)
-        one = bool(mhc.mhc_post_pre_fused(T, n, D, spec.n_splits, 0 if spec.dtype == "bf16" else 1))
-        boundary = {"call": "mhc_post_pre", "one_launch": one,
-                    "traffic": stored_traffic("boundary") if default_wl and one else None,
-                    "us_per_call": us_b, "tokens_per_s": T / (us_b * 1e-6), "algorithmic_bytes": bb,
-                    "gbps": bb / (us_b * 1e-6) / 1e9, "frac_of_peak": bb / (us_b * 1e-6) / 1e9 / PEAK_HBM_GBPS,
-                    "vs_pre_plus_post_step": ms_per_step * 1e3 / us_b}
+    for i in range(args.warmup):
+        run_boundary(i % nsets)
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    for i in range(args.steps):
+        run_boundary(i % nsets)
+    torch.cuda.synchronize()
+    us_b = (time.perf_counter() - t3) * 1e6 / args.steps
+    bb = boundary_bytes(T, n, D, e)
+    one = bool(mhc.mhc_post_pre_fused(T, n, D, spec.n_splits, 0 if spec.dtype == "bf16" else 1))
+    boundary = {"call": "mhc_post_pre", "one_launch": one,
+                "traffic": stored_traffic("boundary") if default_wl and one else None,
+                "us_per_call": us_b, "tokens_per_s": T / (us_b * 1e-6), "algorithmic_bytes": bb,
+                "gbps": bb / (us_b * 1e-6) / 1e9, "frac_of_peak": bb / (us_b * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                "vs_pre_plus_post_step": ms_per_step * 1e3 / us_b}
 
     # practical ceiling: a 1 GiB device-to-device copy kernel on the same stream
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
