@@ -89,6 +89,8 @@ __device__ __forceinline__ u64 count_in(u64* p) {
 // Wait until this wave's outstanding vector memory operations (loads and
 // stores) have completed: vmcnt = 0, other counters unconstrained.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// Wait until this wave's LDS (and scalar memory) operations have completed.
+__device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
 
 }  // namespace
@@ -128,7 +130,7 @@ struct ResShape {
   static constexpr int BBLK = NS * PER_STREAM;     // the slice's B fragments
   static constexpr int kRed = kWaves * 16 * CW;   // per-wave partial rows
   static constexpr int kGs = 16 * 32;             // finalise group sums
-  static constexpr int kScratch = kRed > kGs ? kRed : kGs;
+  static constexpr int kScratch = kRed + kGs;      // per-wave partial rows, then the group sums
   static constexpr size_t lds_bytes = (size_t)BBLK * 1024 + (size_t)kScratch * 4;   // B, then the scratch
   // packing units: (k-step, 8-row k group, VW adjacent fn columns); VW = 4
   // (one 16-byte load per row) when the fn rows keep 16-byte alignment
@@ -373,26 +375,36 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
 
-    // ---- 2. publish the partial rows of this wave's 16 tokens (hi + lo (+ lo2)
-    // columns combined through this wave's part of the scratch)
+    // ---- 2. publish the partial rows of this wave's 16 tokens: hi + lo (+ lo2)
+    // columns combined through this wave's own part of the scratch. The
+    // wave's rows are consecutive tokens, so its 16 (N + 1) words are
+    // contiguous in the exchange buffer: lane l writes words l, l + 64, ...,
+    // and each store instruction covers one contiguous run.
     float* rw = scratch + w * (16 * CW);
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) rw[(q * 4 + i) * CW + cb * 16 + r16] = acc[cb][i];
     if (q == 0) rw[r16 * CW + NCB * 16] = ss;
-    __syncthreads();
-    for (int idx = lane; idx < 16 * (N + 1); idx += 64) {
-      const int r = idx / (N + 1);
-      const int c = idx - r * (N + 1);
-      const int64_t tok = (int64_t)tile * kTM + w * 16 + r;
-      if (tok < T) {
+    wait_lgkm();   // the lanes below read what other lanes of this wave wrote
+    __builtin_amdgcn_wave_barrier();
+    {
+      constexpr int kWords = 16 * (N + 1);
+      const int64_t wrow = (int64_t)tile * kTM + w * 16;   // the wave's first token
+      const int live = T - wrow < 16 ? (int)(T - wrow) * (N + 1) : kWords;   // words of rows below T
+      u64* pw0 = a.part + ((int64_t)sg * T + wrow) * (N + 1);
+#pragma unroll 1
+      for (int idx = lane; idx < live; idx += 64) {
+        const int r = idx / (N + 1);
+        const int c = idx - r * (N + 1);
         const float* rr = rw + r * CW;
-        const float v = c < NS ? rr[c] + rr[c + N] + rr[c + 2 * N] : (c < N ? rr[c] + rr[c + N] : rr[NCB * 16]);
-        put_tagged(a.part + ((int64_t)sg * T + tok) * (N + 1) + c, tag, v);
+        const float hi = rr[c < N ? c : NCB * 16];
+        const float lo = rr[c < N ? c + N : 0];
+        const float lo2 = rr[c < NS ? c + 2 * N : 0];
+        put_tagged(pw0 + idx, tag, c < NS ? hi + lo + lo2 : (c < N ? hi + lo : hi));
       }
     }
-    __syncthreads();   // the scratch is reused below
+    __syncthreads();   // every wave has published before any finalises
     // layer boundary: out goes to HBM now, while the tile's exchange below
     // leaves HBM mostly idle (stored during the GEMM it competed with the
     // residual loads: 8 us more per call at T = 2048, n = 4, D = 7168)
@@ -419,7 +431,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
       // byte offsets from the workspace base fit 32 bits (checked on the host)
       const char* pbase = reinterpret_cast<const char*>(a.part);
       const uint32_t rs8 = (uint32_t)(T * (N + 1) * 8);
-      float* gs = scratch;   // [TB][SUBS][32]
+      float* gs = scratch + F::kRed;   // [TB][SUBS][32], apart from the partial rows
       const long long t0 = wall_clock64();
       for (int m0 = 0; m0 < nmine; m0 += TB) {
         const int m = m0 + mm;
