@@ -25,6 +25,25 @@ __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
+// Per-lane constants of the epilogue: lane e of a 16-lane group scales and
+// biases gate logit e (pre for e < n, post for n <= e < 2n) and comb logit
+// (e / 4, e % 4). Loading them ahead of the epilogue keeps their global loads
+// (and the wait on the memory counter that would also cover every store still
+// in flight) off the finalise path.
+struct EpiConst {
+  float sg, bg;   // gate: hc_scale[0 or 1], bias[e]
+  float sc, bc;   // comb: hc_scale[2], bias[2n + n i + j]
+};
+
+template <int NS>
+__device__ __forceinline__ EpiConst epi_const(const float* __restrict__ hc_scale, const float* __restrict__ bias) {
+  const int e = threadIdx.x & 15;
+  const int i = e >> 2, jj = e & 3;
+  const int cc = (i < NS && jj < NS) ? 2 * NS + i * NS + jj : 0;
+  const int cg = e < 2 * NS ? e : 0;
+  return EpiConst{hc_scale[e < NS ? 0 : 1], bias[cg], hc_scale[2], bias[cc]};
+}
+
 // One 16-lane group handles one token. Lane e of the group holds the reduced
 // column sums c = e (v0) and c = e + 16 (v1) of the token's logit row
 // (N = n(n+2) mixing sums, then the sum of squares at c = N).
@@ -35,9 +54,8 @@ __device__ __forceinline__ float dpp_f32(float v) {
 // (about 1 ulp) instead of dividing. The group must be 16-lane aligned and all
 // 16 lanes must execute the calls (they exchange values within the group).
 template <int NS>
-__device__ __forceinline__ void logits16(float v0, float v1, const float* __restrict__ hc_scale,
-                                         const float* __restrict__ bias, float K, float eps, float& gate, float& zc,
-                                         bool& act) {
+__device__ __forceinline__ void logits16(float v0, float v1, const EpiConst& k, float K, float eps, float& gate,
+                                         float& zc, bool& act) {
   constexpr int N = NS * (NS + 2);
   const int lane = threadIdx.x & 63;
   const int gb = lane & ~15;
@@ -55,8 +73,8 @@ __device__ __forceinline__ void logits16(float v0, float v1, const float* __rest
   const float mc = col(cc);
   const int cg = e < 2 * NS ? e : 0;
   const float mg = col(cg);
-  gate = sigmoidf_ieee(hc_scale[e < NS ? 0 : 1] * (r * mg) + bias[cg]);
-  zc = act ? hc_scale[2] * (r * mc) + bias[cc] : -INFINITY;
+  gate = sigmoidf_ieee(k.sg * (r * mg) + k.bg);
+  zc = act ? k.sc * (r * mc) + k.bc : -INFINITY;
 }
 
 __device__ __forceinline__ float sinkhorn16(float zc, bool act, int repeat) {
@@ -77,12 +95,11 @@ __device__ __forceinline__ float sinkhorn16(float zc, bool act, int repeat) {
 }
 
 template <int NS>
-__device__ __forceinline__ void epilogue16(float v0, float v1, const float* __restrict__ hc_scale,
-                                           const float* __restrict__ bias, float K, float eps, int repeat,
+__device__ __forceinline__ void epilogue16(float v0, float v1, const EpiConst& k, float K, float eps, int repeat,
                                            float& gate, float& comb) {
   float zc;
   bool act;
-  logits16<NS>(v0, v1, hc_scale, bias, K, eps, gate, zc, act);
+  logits16<NS>(v0, v1, k, K, eps, gate, zc, act);
   comb = sinkhorn16(zc, act, repeat);
 }
 

@@ -307,6 +307,7 @@ __global__ __launch_bounds__(kEpiThreads) void pre_epilogue_kernel(
     // sum of squares is column N) in ascending split order; the loads of each
     // group of 8 splits are in flight together. Lanes 16..63 repeat lane & 15.
     const int e = tid & 15;
+    const EpiConst kc = epi_const<NS>(hc_scale, bias);
     const float* pt = part + t * NP;
     const int64_t sstride = T * NP;
     float v0 = 0.0f, v1 = 0.0f;
@@ -325,7 +326,7 @@ __global__ __launch_bounds__(kEpiThreads) void pre_epilogue_kernel(
       }
     }
     float gate, combv;
-    epilogue16<NS>(v0, v1, hc_scale, bias, (float)(NS * D), eps, repeat, gate, combv);
+    epilogue16<NS>(v0, v1, kc, (float)(NS * D), eps, repeat, gate, combv);
     if (tid < NS) pre_s[tid] = gate;
     else if (tid < 2 * NS) post[t * NS + (tid - NS)] = gate;
     if (tid < 16 && (e >> 2) < NS && (e & 3) < NS) comb[t * NS * NS + (e >> 2) * NS + (e & 3)] = combv;

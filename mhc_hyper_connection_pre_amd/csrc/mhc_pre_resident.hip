@@ -432,6 +432,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
       const char* pbase = reinterpret_cast<const char*>(a.part);
       const uint32_t rs8 = (uint32_t)(T * (N + 1) * 8);
       float* gs = scratch + F::kRed;   // [TB][SUBS][32], apart from the partial rows
+      const EpiConst kc = epi_const<NS>(a.hc_scale, a.bias);
       const long long t0 = wall_clock64();
       for (int m0 = 0; m0 < nmine; m0 += TB) {
         const int m = m0 + mm;
@@ -439,13 +440,16 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
         const bool ok = m < nmine && tok < T && c <= N;
         const uint32_t off0 = ok ? (uint32_t)((tok * (N + 1) + c) * 8) : 0u;
         float accm = 0.0f;
+        // words past the splits count as ready; a poll re-reads only the
+        // words not yet ready, so waiting adds little fabric traffic
+        u64 vv[kLoads];
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) vv[u] = (u64)((ok && sub + SUBS * u < S) ? tag ^ 1u : tag) << 32;
         for (;;) {
-          u64 vv[kLoads];
 #pragma unroll
           for (int u = 0; u < kLoads; ++u) {
             const int sp = sub + SUBS * u;
-            vv[u] = (ok && sp < S) ? ld_agent(reinterpret_cast<const u64*>(pbase + off0 + (uint32_t)sp * rs8))
-                                   : ((u64)tag << 32);
+            if (!tag_is(vv[u], tag)) vv[u] = ld_agent(reinterpret_cast<const u64*>(pbase + off0 + (uint32_t)sp * rs8));
           }
           bool ready = true;
           accm = 0.0f;
@@ -474,7 +478,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
             }
           float gate, zc;
           bool act;
-          logits16<NS>(v0, v1, a.hc_scale, a.bias, a.K, a.eps, gate, zc, act);
+          logits16<NS>(v0, v1, kc, a.K, a.eps, gate, zc, act);
           const int64_t tk = (int64_t)tile * kTM + sg + (int64_t)S * (m0 + tt);
           const bool mine = tt < TB && m0 + tt < nmine && tk < T;
           // pre first: the other workgroups of the tile wait for it, not for comb
@@ -494,13 +498,16 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
     {
       const u64* pp = a.prebuf + (rok ? row : 0) * 4;
       const long long t0 = wall_clock64();
+      u64 wv[NS];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) wv[i] = (u64)(rok ? tag ^ 1u : tag) << 32;
       for (;;) {
         bool ready = true;
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
-          const u64 wv = rok ? ld_agent(pp + i) : ((u64)tag << 32);
-          ready = ready && tag_is(wv, tag);
-          pre[i] = tag_val(wv);
+          if (!tag_is(wv[i], tag)) wv[i] = ld_agent(pp + i);
+          ready = ready && tag_is(wv[i], tag);
+          pre[i] = tag_val(wv[i]);
         }
         if (__all(ready)) break;
         if (wall_clock64() - t0 > kPollTicks) {
