@@ -23,9 +23,9 @@
  *  - `dt` is the storage type of the residual-shaped tensors (residual, h,
  *    y, out, normalized). post, comb, fn, hc_scale, bias, combine_w and
  *    norm_weight are always float32.
- *  - Supported on the GPU: 1 <= n <= 4; D a multiple of 8 (bf16) or 4 (f32);
- *    residual-shaped pointers 16-byte aligned; float32 pointers 4-byte
- *    aligned. T = 0 is a successful no-op.
+ *  - Supported on the GPU: 1 <= n <= 4 and n = 8; D a multiple of 8 (bf16)
+ *    or 4 (f32); residual-shaped pointers 16-byte aligned; float32 pointers
+ *    4-byte aligned. T = 0 is a successful no-op.
  *  - Errors: argument problems return a negative status before anything is
  *    launched, and no output is touched. A failed launch returns
  *    MHC_ERR_HIP; mhc_last_error() then describes it. Nothing is printed and
@@ -49,7 +49,7 @@ extern "C" {
 typedef enum {
   MHC_OK = 0,
   MHC_ERR_INVALID_ARG = -1,  /* null pointer, negative size, bad eps/repeat/dtype */
-  MHC_ERR_UNSUPPORTED = -2,  /* valid mathematically but not built (n > 4, D too large) */
+  MHC_ERR_UNSUPPORTED = -2,  /* valid mathematically but not built (n = 5..7 or > 8, D too large) */
   MHC_ERR_MISALIGNED = -3,   /* D not a multiple of the vector width, or a pointer misaligned */
   MHC_ERR_WORKSPACE = -4,    /* workspace missing, misaligned or smaller than required */
   MHC_ERR_HIP = -5           /* a HIP launch failed */
@@ -101,7 +101,7 @@ MHC_API size_t mhc_pre_workspace_bytes(int64_t T, int n, int64_t D, int n_splits
  *   reassociation, and a fixed value is bitwise repeatable.
  * Paths: the single-pass kernel (one launch; the residual is read once and
  *   stays in registers; the workgroups of a token tile exchange partial sums
- *   through the workspace) covers bf16 with D a multiple of 32 for which a
+ *   through the workspace) covers bf16, n <= 4, D a multiple of 32 for which a
  *   slice tiling fits (mhc_pre_splits(..., -1, ...) > 0) and a 16-byte
  *   aligned fn; n_splits = 0 takes it when it can. Otherwise the two-pass
  *   path runs (pack fn, split-K GEMM, then an epilogue that reads the

@@ -30,7 +30,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 int check_shape(int64_t T, int n, int64_t D, mhc_dtype dt) {
   if (dt != MHC_BF16 && dt != MHC_F32) return MHC_ERR_INVALID_ARG;
   if (T < 0 || n < 1 || D < 1) return MHC_ERR_INVALID_ARG;
-  if (n > 4) return MHC_ERR_UNSUPPORTED;
+  if (n > 4 && n != 8) return MHC_ERR_UNSUPPORTED;
   if (D % vec_elems(dt) != 0) return MHC_ERR_MISALIGNED;
   // grid.x is the token count; keep every byte offset far from int64 overflow
   if (T > 0x7fffffffLL || D > (1LL << 26)) return MHC_ERR_UNSUPPORTED;
@@ -56,7 +56,10 @@ int make_pre_plan(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, PrePl
   q.ksteps = (int)((q.K + kstep - 1) / kstep);
   if (dt == MHC_BF16) {
     q.NCB = pack_blocks(n);
-    if (n_splits == 1) {  // one split: a tall workgroup of 16 waves per 16 tokens keeps the k-loop parallel
+    if (n == 8) {   // 11 column blocks: one 16-token tile per wave, four waves (LDS for the wave sums)
+      q.MT = 1;
+      q.NW = 4;
+    } else if (n_splits == 1) {  // one split: a tall workgroup of 16 waves per 16 tokens keeps the k-loop parallel
       q.MT = 1;
       q.NW = 16;
     } else {

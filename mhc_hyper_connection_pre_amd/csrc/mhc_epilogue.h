@@ -1,5 +1,6 @@
-// Per-token epilogue of mhc_pre on 16 lanes of a wave: RMS factor, hc_scale,
-// bias, sigmoid gates and the Sinkhorn normalisation of the comb logits.
+// Per-token epilogue of mhc_pre on 16 lanes of a wave (n <= 4) or on a whole
+// wave (n <= 8): RMS factor, hc_scale, bias, sigmoid gates and the Sinkhorn
+// normalisation of the comb logits.
 //
 // The pre call of sglang PR #24355 analysis ("AMD ROCm DeepSeek-V4
 // performance optimisation: Aiter MHC kernel integration"), section 2, returns
@@ -101,6 +102,72 @@ __device__ __forceinline__ void epilogue16(float v0, float v1, const EpiConst& k
   bool act;
   logits16<NS>(v0, v1, k, K, eps, gate, zc, act);
   comb = sinkhorn16(zc, act, repeat);
+}
+
+// The same epilogue for up to 8 streams on a whole wave (one token per wave).
+// Lane l brings the column sums c = l (v0) and c = l + 64 (v1) of the token's
+// logit row (the sum of squares at c = N). Lane e holds gate logit e for
+// e < 2n and comb entry (e / 8, e % 8) of an 8 x 8 padded layout: a comb row is
+// 8 consecutive lanes (xor 1, 2, 4), a column is lanes j, j + 8, ..., j + 56
+// (xor 8, 16, 32). All 64 lanes must execute the calls.
+template <int NS>
+__device__ __forceinline__ EpiConst epi_const64(const float* __restrict__ hc_scale,
+                                                const float* __restrict__ bias) {
+  const int e = threadIdx.x & 63;
+  const int i = e >> 3, jj = e & 7;
+  const int cc = (i < NS && jj < NS) ? 2 * NS + i * NS + jj : 0;
+  const int cg = e < 2 * NS ? e : 0;
+  return EpiConst{hc_scale[e < NS ? 0 : 1], bias[cg], hc_scale[2], bias[cc]};
+}
+
+template <int NS>
+__device__ __forceinline__ void logits64(float v0, float v1, const EpiConst& k, float K, float eps, float& gate,
+                                         float& zc, bool& act) {
+  constexpr int N = NS * (NS + 2);
+  static_assert(N < 128, "two column sums per lane");
+  const int e = threadIdx.x & 63;
+  auto col = [&](int c) {  // column sum c of the token
+    const float a = __shfl(v0, c & 63);
+    const float b = __shfl(v1, c & 63);
+    return c < 64 ? a : b;
+  };
+  const float ssq = col(N);
+  const float r = 1.0f / sqrtf(ssq / K + eps);
+  const int i = e >> 3, jj = e & 7;
+  act = i < NS && jj < NS;
+  const int cc = act ? 2 * NS + i * NS + jj : 0;
+  const float mc = col(cc);
+  const int cg = e < 2 * NS ? e : 0;
+  const float mg = col(cg);
+  gate = sigmoidf_ieee(k.sg * (r * mg) + k.bg);
+  zc = act ? k.sc * (r * mc) + k.bc : -INFINITY;
+}
+
+__device__ __forceinline__ float sinkhorn64(float zc, bool act, int repeat) {
+  float rmax = fmaxf(zc, __shfl_xor(zc, 1));
+  rmax = fmaxf(rmax, __shfl_xor(rmax, 2));
+  rmax = fmaxf(rmax, __shfl_xor(rmax, 4));
+  float M = act ? expf(zc - rmax) : 0.0f;
+  for (int it = 0; it < repeat; ++it) {
+    float rs = M + __shfl_xor(M, 1);
+    rs = rs + __shfl_xor(rs, 2);
+    rs = rs + __shfl_xor(rs, 4);
+    M = act ? M * __builtin_amdgcn_rcpf(rs) : 0.0f;
+    float cs = M + __shfl_xor(M, 8);
+    cs = cs + __shfl_xor(cs, 16);
+    cs = cs + __shfl_xor(cs, 32);
+    M = act ? M * __builtin_amdgcn_rcpf(cs) : 0.0f;
+  }
+  return M;
+}
+
+template <int NS>
+__device__ __forceinline__ void epilogue64(float v0, float v1, const EpiConst& k, float K, float eps, int repeat,
+                                           float& gate, float& comb) {
+  float zc;
+  bool act;
+  logits64<NS>(v0, v1, k, K, eps, gate, zc, act);
+  comb = sinkhorn64(zc, act, repeat);
 }
 
 }  // namespace mhc

@@ -21,13 +21,17 @@
 namespace mhc {
 
 constexpr int kPackSteps = 2;   // k-steps (32 fn rows each) per 256-thread block
-constexpr int kPackMaxN = 24;   // n <= 4
+constexpr int kPackMaxN = 80;   // n <= 8
 
 // 16-column blocks of [hi | lo | lo2 of the pre columns] for n streams.
 __host__ __device__ constexpr int pack_blocks(int n) { return (2 * n * (n + 2) + n + 15) / 16; }
 
 // n from N = n (n + 2).
-__host__ __device__ constexpr int n_pre(int N) { return N == 3 ? 1 : (N == 8 ? 2 : (N == 15 ? 3 : 4)); }
+__host__ __device__ constexpr int n_pre(int N) {
+  int n = 1;
+  while (n * (n + 2) < N) ++n;
+  return n;
+}
 
 // Part `part` (0 = hi, 1 = lo, 2 = lo2) of the three-term bf16 split of x,
 // as a float (exactly representable in bf16); part 3 is a zero column.
@@ -79,13 +83,14 @@ __device__ __forceinline__ void pack_fn_block(const float* __restrict__ fn, u32x
     }
   }
   __syncthreads();
+  const int npre = n_pre(N);
   for (int f = threadIdx.x; f < kPackSteps * NCB * 64; f += blockDim.x) {
     const int sl = f / (NCB * 64);
     const int cb = (f / 64) % NCB;
     const int lane = f & 63;
     if (s0 + sl >= ksteps) continue;
     const int col = cb * 16 + (lane & 15);
-    const int part = col < N ? 0 : (col < 2 * N ? 1 : (col < 2 * N + n_pre(N) ? 2 : 3));
+    const int part = col < N ? 0 : (col < 2 * N ? 1 : (col < 2 * N + npre ? 2 : 3));
     const int c = col - part * N;
     float v[8];
 #pragma unroll

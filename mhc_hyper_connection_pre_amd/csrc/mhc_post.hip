@@ -82,18 +82,24 @@ static hipError_t launch_post_n(const void* h, const void* residual, const float
                                 void* out, int64_t T, int64_t D, hipStream_t s) {
   typedef typename S::elem E;
   const int64_t nch = D / S::V;
+  constexpr int kMaxCpt = NS > 4 ? 2 : 4;   // vectors in flight per thread: (n + 1) x CPT x 4 registers
   int cpt = (int)((nch + kPostThreads - 1) / kPostThreads);
-  cpt = cpt < 1 ? 1 : (cpt > 4 ? 4 : cpt);
+  cpt = cpt < 1 ? 1 : (cpt > kMaxCpt ? kMaxCpt : cpt);
   const dim3 grid((unsigned)T), block(kPostThreads);
   E* o = static_cast<E*>(out);
   const E* hh = static_cast<const E*>(h);
   const E* x = static_cast<const E*>(residual);
 #define MHC_POST(C) hipLaunchKernelGGL((post_kernel<S, NS, C>), grid, block, 0, s, o, hh, x, post, comb, D)
-  switch (cpt) {
-    case 1: MHC_POST(1); break;
-    case 2: MHC_POST(2); break;
-    case 3: MHC_POST(3); break;
-    default: MHC_POST(4); break;
+  if constexpr (kMaxCpt == 2) {
+    if (cpt == 1) MHC_POST(1);
+    else MHC_POST(2);
+  } else {
+    switch (cpt) {
+      case 1: MHC_POST(1); break;
+      case 2: MHC_POST(2); break;
+      case 3: MHC_POST(3); break;
+      default: MHC_POST(4); break;
+    }
   }
 #undef MHC_POST
   return hipGetLastError();
@@ -106,6 +112,7 @@ static hipError_t launch_post_s(const void* h, const void* residual, const float
     case 1: return launch_post_n<S, 1>(h, residual, post, comb, out, T, D, s);
     case 2: return launch_post_n<S, 2>(h, residual, post, comb, out, T, D, s);
     case 3: return launch_post_n<S, 3>(h, residual, post, comb, out, T, D, s);
+    case 8: return launch_post_n<S, 8>(h, residual, post, comb, out, T, D, s);
     default: return launch_post_n<S, 4>(h, residual, post, comb, out, T, D, s);
   }
 }
@@ -244,6 +251,7 @@ static hipError_t launch_pcn_s(void* normalized, void* out, const void* h, const
     case 1: return launch_pcn_n<S, 1>(normalized, out, h, residual, post, comb, w, g, eps, T, D, s);
     case 2: return launch_pcn_n<S, 2>(normalized, out, h, residual, post, comb, w, g, eps, T, D, s);
     case 3: return launch_pcn_n<S, 3>(normalized, out, h, residual, post, comb, w, g, eps, T, D, s);
+    case 8: return launch_pcn_n<S, 8>(normalized, out, h, residual, post, comb, w, g, eps, T, D, s);
     default: return launch_pcn_n<S, 4>(normalized, out, h, residual, post, comb, w, g, eps, T, D, s);
   }
 }

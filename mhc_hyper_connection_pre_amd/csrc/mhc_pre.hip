@@ -162,6 +162,7 @@ __global__ __launch_bounds__(NW * 64) void pre_gemm_bf16_kernel(const uint16_t* 
   // partial[split][token][c] = sum over waves of (hi + lo (+ lo2 for the
   // first n columns)) for c < N, squares at c = N.
   const int outs = MT * 16 * (N + 1);
+  const int npre = n_pre(N);
   for (int idx = threadIdx.x; idx < outs; idx += NW * 64) {
     const int row = idx / (N + 1);
     const int c = idx - row * (N + 1);
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(NW * 64) void pre_gemm_bf16_kernel(const uint16_t* 
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) {
         const float* r = red + ww * (MT * 16 * CW) + row * CW;
-        v += c < n_pre(N) ? r[c] + r[c + N] + r[c + 2 * N] : r[c] + r[c + N];
+        v += c < npre ? r[c] + r[c + N] + r[c + 2 * N] : r[c] + r[c + N];
       }
     } else {
 #pragma unroll
@@ -184,8 +185,8 @@ __global__ __launch_bounds__(NW * 64) void pre_gemm_bf16_kernel(const uint16_t* 
 
 // ------------------------------------------------------------------ f32 GEMM
 // One wave per (token, split); lanes stride over k; butterfly reduction.
-constexpr int kF32MaxN = 24;
-
+// kF32MaxN: N = n (n + 2) sums per lane (24 for n <= 4, 80 for n = 8).
+template <int kF32MaxN>
 __global__ __launch_bounds__(256) void pre_gemm_f32_kernel(const float* __restrict__ x, const float* __restrict__ fn,
                                                            float* __restrict__ part, int64_t T, int64_t K, int N,
                                                            int NP, int64_t k_per_split) {
@@ -223,28 +224,21 @@ __global__ __launch_bounds__(256) void pre_gemm_f32_kernel(const float* __restri
   }
 }
 
+template <int MT, int NW, int NCB>
+static void launch_gemm_bf16(const PrePlan& p, const uint16_t* x, const u32x4* fnp, float* part, hipStream_t s) {
+  const dim3 grid((unsigned)((p.T + 16 * MT - 1) / (16 * MT)), (unsigned)p.S);
+  hipLaunchKernelGGL((pre_gemm_bf16_kernel<MT, NW, NCB>), grid, dim3(NW * 64), 0, s, x, fnp, part, p.T, p.K, p.N,
+                     p.NP, p.ksteps, p.steps_per_split);
+}
+
 template <int MT, int NW>
 static hipError_t launch_gemm_bf16_ncb(const PrePlan& p, const uint16_t* x, const u32x4* fnp, float* part,
                                        hipStream_t s) {
-  const dim3 grid((unsigned)((p.T + 16 * MT - 1) / (16 * MT)), (unsigned)p.S);
-  const dim3 block(NW * 64);
   switch (p.NCB) {
-    case 1:
-      hipLaunchKernelGGL((pre_gemm_bf16_kernel<MT, NW, 1>), grid, block, 0, s, x, fnp, part, p.T, p.K, p.N, p.NP,
-                         p.ksteps, p.steps_per_split);
-      break;
-    case 2:
-      hipLaunchKernelGGL((pre_gemm_bf16_kernel<MT, NW, 2>), grid, block, 0, s, x, fnp, part, p.T, p.K, p.N, p.NP,
-                         p.ksteps, p.steps_per_split);
-      break;
-    case 3:
-      hipLaunchKernelGGL((pre_gemm_bf16_kernel<MT, NW, 3>), grid, block, 0, s, x, fnp, part, p.T, p.K, p.N, p.NP,
-                         p.ksteps, p.steps_per_split);
-      break;
-    default:
-      hipLaunchKernelGGL((pre_gemm_bf16_kernel<MT, NW, 4>), grid, block, 0, s, x, fnp, part, p.T, p.K, p.N, p.NP,
-                         p.ksteps, p.steps_per_split);
-      break;
+    case 1: launch_gemm_bf16<MT, NW, 1>(p, x, fnp, part, s); break;
+    case 2: launch_gemm_bf16<MT, NW, 2>(p, x, fnp, part, s); break;
+    case 3: launch_gemm_bf16<MT, NW, 3>(p, x, fnp, part, s); break;
+    default: launch_gemm_bf16<MT, NW, 4>(p, x, fnp, part, s); break;
   }
   return hipGetLastError();
 }
@@ -254,12 +248,19 @@ hipError_t launch_pre_gemm(const PrePlan& p, const void* residual, const void* f
   if (p.dt == MHC_F32) {
     const dim3 grid((unsigned)((p.T + 3) / 4), (unsigned)p.S);
     const int64_t kps = (int64_t)p.steps_per_split * 64;
-    hipLaunchKernelGGL(pre_gemm_f32_kernel, grid, dim3(256), 0, s, static_cast<const float*>(residual), fn, part,
-                       p.T, p.K, p.N, p.NP, kps);
+    const float* x = static_cast<const float*>(residual);
+    if (p.N <= 24)
+      hipLaunchKernelGGL(pre_gemm_f32_kernel<24>, grid, dim3(256), 0, s, x, fn, part, p.T, p.K, p.N, p.NP, kps);
+    else
+      hipLaunchKernelGGL(pre_gemm_f32_kernel<80>, grid, dim3(256), 0, s, x, fn, part, p.T, p.K, p.N, p.NP, kps);
     return hipGetLastError();
   }
   const uint16_t* x = static_cast<const uint16_t*>(residual);
   const u32x4* f = static_cast<const u32x4*>(fnp);
+  if (p.n == 8) {   // 11 column blocks: one 16-token tile per wave, four waves
+    launch_gemm_bf16<1, 4, pack_blocks(8)>(p, x, f, part, s);
+    return hipGetLastError();
+  }
   if (p.MT == 1) return launch_gemm_bf16_ncb<1, 16>(p, x, f, part, s);
   return launch_gemm_bf16_ncb<4, 4>(p, x, f, part, s);
 }
@@ -268,7 +269,8 @@ hipError_t launch_pre_gemm(const PrePlan& p, const void* residual, const void* f
 // One 256-thread workgroup per token. The token row (n streams x D) is
 // prefetched in 16-byte vectors first; wave 0 meanwhile reduces the split
 // partials and runs the gates and Sinkhorn with lane e = 4 i + j holding
-// comb[i][j] (rows: xor 1, 2; columns: xor 4, 8; padded to 4 x 4 for n < 4).
+// comb[i][j] (rows: xor 1, 2; columns: xor 4, 8; padded to 4 x 4 for n < 4),
+// or, for n = 8, lane e = 8 i + j on the whole wave.
 constexpr int kEpiThreads = 256;
 
 template <class S, int NS, int CPT>
@@ -303,11 +305,14 @@ __global__ __launch_bounds__(kEpiThreads) void pre_epilogue_kernel(
   }
 
   if (tid < kWave) {
-    // Lane e of wave 0 sums columns e and e + 16 of the split partials (the
+    // Lane e of wave 0 sums columns e and e + CS of the split partials (the
     // sum of squares is column N) in ascending split order; the loads of each
-    // group of 8 splits are in flight together. Lanes 16..63 repeat lane & 15.
-    const int e = tid & 15;
-    const EpiConst kc = epi_const<NS>(hc_scale, bias);
+    // group of 8 splits are in flight together. CS = 16 lanes run the epilogue
+    // for n <= 4 (lanes 16..63 repeat lane & 15), the whole wave for n = 8.
+    constexpr bool kWide = NS > 4;
+    constexpr int CS = kWide ? 64 : 16;
+    const int e = tid & (CS - 1);
+    const EpiConst kc = kWide ? epi_const64<NS>(hc_scale, bias) : epi_const<NS>(hc_scale, bias);
     const float* pt = part + t * NP;
     const int64_t sstride = T * NP;
     float v0 = 0.0f, v1 = 0.0f;
@@ -317,7 +322,7 @@ __global__ __launch_bounds__(kEpiThreads) void pre_epilogue_kernel(
       for (int u = 0; u < 8; ++u) {
         const bool in = sp0 + u < nsplit;
         a0[u] = (in && e <= N) ? pt[(int64_t)(sp0 + u) * sstride + e] : 0.0f;
-        a1[u] = (in && e + 16 <= N) ? pt[(int64_t)(sp0 + u) * sstride + e + 16] : 0.0f;
+        a1[u] = (in && e + CS <= N) ? pt[(int64_t)(sp0 + u) * sstride + e + CS] : 0.0f;
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -326,10 +331,15 @@ __global__ __launch_bounds__(kEpiThreads) void pre_epilogue_kernel(
       }
     }
     float gate, combv;
-    epilogue16<NS>(v0, v1, kc, (float)(NS * D), eps, repeat, gate, combv);
+    if constexpr (kWide) {
+      epilogue64<NS>(v0, v1, kc, (float)(NS * D), eps, repeat, gate, combv);
+    } else {
+      epilogue16<NS>(v0, v1, kc, (float)(NS * D), eps, repeat, gate, combv);
+    }
     if (tid < NS) pre_s[tid] = gate;
     else if (tid < 2 * NS) post[t * NS + (tid - NS)] = gate;
-    if (tid < 16 && (e >> 2) < NS && (e & 3) < NS) comb[t * NS * NS + (e >> 2) * NS + (e & 3)] = combv;
+    constexpr int RW = kWide ? 8 : 4;   // lanes per row of the padded comb layout
+    if (tid < RW * RW && e / RW < NS && e % RW < NS) comb[t * NS * NS + (e / RW) * NS + e % RW] = combv;
   }
   __syncthreads();
 
@@ -380,19 +390,25 @@ static hipError_t launch_epi_n(const PrePlan& p, const void* residual, const flo
                                unsigned long long* status, hipStream_t s) {
   typedef typename S::elem E;
   const int64_t nch = p.D / S::V;
+  constexpr int kMaxCpt = NS > 4 ? 2 : 4;   // prefetched vectors per thread: n x CPT x 4 registers
   int cpt = (int)((nch + kEpiThreads - 1) / kEpiThreads);
-  cpt = cpt < 1 ? 1 : (cpt > 4 ? 4 : cpt);
+  cpt = cpt < 1 ? 1 : (cpt > kMaxCpt ? kMaxCpt : cpt);
   const dim3 grid((unsigned)p.T), block(kEpiThreads);
   const E* x = static_cast<const E*>(residual);
   E* yy = static_cast<E*>(y);
 #define MHC_EPI(C)                                                                                                 \
   hipLaunchKernelGGL((pre_epilogue_kernel<S, NS, C>), grid, block, 0, s, x, part, p.S, p.NP, hc_scale, bias, post, \
                      comb, yy, p.T, p.D, repeat, eps, status)
-  switch (cpt) {
-    case 1: MHC_EPI(1); break;
-    case 2: MHC_EPI(2); break;
-    case 3: MHC_EPI(3); break;
-    default: MHC_EPI(4); break;
+  if constexpr (kMaxCpt == 2) {
+    if (cpt == 1) MHC_EPI(1);
+    else MHC_EPI(2);
+  } else {
+    switch (cpt) {
+      case 1: MHC_EPI(1); break;
+      case 2: MHC_EPI(2); break;
+      case 3: MHC_EPI(3); break;
+      default: MHC_EPI(4); break;
+    }
   }
 #undef MHC_EPI
   return hipGetLastError();
@@ -406,6 +422,7 @@ static hipError_t launch_epi_s(const PrePlan& p, const void* residual, const flo
     case 1: return launch_epi_n<S, 1>(p, residual, part, hc_scale, bias, post, comb, y, repeat, eps, status, s);
     case 2: return launch_epi_n<S, 2>(p, residual, part, hc_scale, bias, post, comb, y, repeat, eps, status, s);
     case 3: return launch_epi_n<S, 3>(p, residual, part, hc_scale, bias, post, comb, y, repeat, eps, status, s);
+    case 8: return launch_epi_n<S, 8>(p, residual, part, hc_scale, bias, post, comb, y, repeat, eps, status, s);
     default: return launch_epi_n<S, 4>(p, residual, part, hc_scale, bias, post, comb, y, repeat, eps, status, s);
   }
 }

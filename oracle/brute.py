@@ -5,7 +5,7 @@ sources, [P1] sglang PR #24355 analysis sections 2-3 and [P2] sglang PR #39704
 analysis section 1, and for the readings), written token by token and element
 by element with ``math`` and Python floats, no numpy. It exists to pin the
 vectorised oracle: a transposed einsum, a wrong axis or a broadcast slip there
-shows up as a disagreement here. Tiny shapes only (T <= 4, n <= 4, D <= 16).
+shows up as a disagreement here. Tiny shapes only (T <= 4, n <= 8, D <= 16).
 
 Inputs are nested Python lists (or anything indexable) of float64 values that
 are already decoded from storage; outputs are float64 and unrounded.

@@ -49,10 +49,10 @@ def _pre_all(O, x, fn, hc, bias, n, R, eps=EPS):
 # ---------------------------------------------------------------- brute force
 
 def pin_brute_pre(O):
-    """Whole pre pipeline vs scalar loops, T <= 3, n in 1..4, D <= 8, random R."""
+    """Whole pre pipeline vs scalar loops, T <= 3, n in 1..4 and 8, D <= 8, random R."""
     g = np.random.default_rng(11)
-    for case in range(16):
-        n = 1 + case % 4
+    for case in range(18):
+        n = 1 + case % 4 if case < 16 else 8
         D = (1, 2, 3, 8)[(case // 4) % 4]
         T = 1 + case % 3
         R = int(g.integers(1, 7))
@@ -67,7 +67,7 @@ def pin_brute_pre(O):
 def pin_brute_post(O):
     """mhc_post mix vs scalar loops; orientation of comb included."""
     g = np.random.default_rng(12)
-    for n in (1, 2, 3, 4):
+    for n in (1, 2, 3, 4, 8):
         T, D = 2, 5
         x = g.standard_normal((T, n, D))
         h = g.standard_normal((T, D))

@@ -65,6 +65,10 @@ def test_pre_validation(L):
     assert pre(L, T=-1) == INVALID
     assert pre(L, n=0) == INVALID
     assert pre(L, n=5) == UNSUPPORTED
+    assert pre(L, n=7) == UNSUPPORTED
+    assert pre(L, n=9) == UNSUPPORTED
+    assert pre(L, n=8, T=0) == OK                  # n = 8: built (two-pass path)
+    assert pre(L, n=8, splits=-1) == UNSUPPORTED   # ... but not on the single-pass kernel
     assert pre(L, D=0) == INVALID
     assert pre(L, D=12) == MISALIGNED               # bf16 needs D % 8 == 0
     assert pre(L, D=12, dt=F32, T=0) == OK          # f32 needs D % 4 == 0
@@ -117,6 +121,14 @@ def test_pre_plan(L):
     assert L.mhc_pre_splits(T, n, D, -2, BF16) == INVALID
     # fp32 residuals always take the two-pass path (no packed fn)
     assert L.mhc_pre_workspace_bytes(8, 4, 256, 0, F32) == 256 + (L.mhc_pre_splits(8, 4, 256, 0, F32) * 8 * 28 * 4 + 255) // 256 * 256
+    # n = 8 (N = 80): two-pass only; [hi | lo | lo2 of the 8 pre columns] = 168 -> 11 blocks; partials [S, T, 84]
+    T8, D8 = 64, 1024
+    assert L.mhc_pre_splits(T8, 8, D8, -1, BF16) == UNSUPPORTED
+    S8 = L.mhc_pre_splits(T8, 8, D8, 0, BF16)
+    assert S8 >= 1 and L.mhc_pre_splits(T8, 8, D8, 4, BF16) == 4
+    fnp8 = (8 * D8 // 32) * 11 * 1024
+    assert L.mhc_pre_workspace_bytes(T8, 8, D8, 4, BF16) == 256 + fnp8 + (4 * T8 * 84 * 4 + 255) // 256 * 256
+    assert L.mhc_post_pre_fused(T8, 8, D8, 0, BF16) == 0
 
 
 def test_post_validation(L):
@@ -125,6 +137,7 @@ def test_post_validation(L):
     assert post(T=0) == OK
     assert post(T=-3) == INVALID
     assert post(n=5) == UNSUPPORTED
+    assert post(n=8, T=0) == OK
     assert post(D=4) == MISALIGNED
     assert post(out=None) == INVALID
     assert post(h=A + 4) == MISALIGNED
@@ -167,6 +180,8 @@ def test_post_combine_norm_validation(L):
         return L.mhc_post_combine_norm(nz, out, h, res, p, c, w, g, eps, dt, T, n, D, None)
     assert pcn(T=0) == OK
     assert pcn(T=0, out=None) == OK
+    assert pcn(n=6) == UNSUPPORTED
+    assert pcn(n=8, T=0) == OK
     assert pcn(eps=0.0) == INVALID
     assert pcn(nz=None) == INVALID
     assert pcn(w=None) == INVALID

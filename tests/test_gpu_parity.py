@@ -73,7 +73,7 @@ def _check_post(x, g, post_np, comb_np, tokens=None, what=""):
 # ---------------------------------------------------------------- small, ragged, every n and dtype
 
 SMALL = [(T, n, D, dt, sp) for (T, n, D) in ((1, 4, 8), (7, 4, 264), (33, 4, 1032), (67, 3, 520),
-                                             (130, 2, 2056), (17, 1, 72), (5, 4, 4104))
+                                             (130, 2, 2056), (17, 1, 72), (5, 4, 4104), (3, 8, 520), (66, 8, 1032))
          for dt in ("bf16", "f32") for sp in (0, 1, 3)]
 
 
@@ -198,7 +198,8 @@ def test_single_pass_graph_replay():
 
 
 @pytest.mark.parametrize("T,n,D,dt", [(3, 4, 64, "bf16"), (65, 4, 5120, "bf16"), (9, 2, 1024, "f32"),
-                                      (4, 1, 32768, "bf16"), (2, 4, 16384, "f32")])
+                                      (4, 1, 32768, "bf16"), (2, 4, 16384, "f32"), (3, 8, 64, "bf16"),
+                                      (64, 8, 5120, "bf16"), (5, 8, 1024, "f32")])
 def test_small_post_combine_norm(T, n, D, dt):
     x = W.generate(W.custom(T, n, D, dt, seed=5 + T + D, combine=True))
     g = _gpu_inputs(x)
@@ -371,6 +372,17 @@ def test_error_paths_on_gpu():
         mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"],
                     workspace=torch.empty(256, dtype=torch.uint8, device="cuda"))
     assert e.value.status == -4
+    # n = 8 runs on the two-pass kernels only; n = 5 is not built
+    x8 = W.generate(W.custom(4, 8, 64, "bf16", seed=3))
+    g8 = _gpu_inputs(x8)
+    with pytest.raises(mhc.MhcError) as e:
+        mhc.mhc_pre(g8["residual"], g8["fn"], g8["hc_scale"], g8["bias"], n_splits=-1)
+    assert e.value.status == -2
+    x5 = W.generate(W.custom(4, 5, 64, "bf16", seed=3))
+    g5 = _gpu_inputs(x5)
+    with pytest.raises(mhc.MhcError) as e:
+        mhc.mhc_pre(g5["residual"], g5["fn"], g5["hc_scale"], g5["bias"])
+    assert e.value.status == -2
     # T = 0 is a no-op
     z = torch.empty((0, 4, 64), dtype=torch.bfloat16, device="cuda")
     p, c, y = mhc.mhc_pre(z, g["fn"], g["hc_scale"], g["bias"])
