@@ -63,8 +63,9 @@ MHC_API const char* mhc_status_string(int status);
 /* Text of the last HIP error seen by this thread (static storage, "" if none). */
 MHC_API const char* mhc_last_error(void);
 
-/* Number of split-K partials mhc_pre uses for these sizes: `n_splits` itself
- * when positive, otherwise the library's choice for the shape. Returns a
+/* Number of split-K partials (slices of the hidden axis) mhc_pre uses for
+ * these sizes: `n_splits` itself when positive (capped at K / 32), S for
+ * n_splits = -S, otherwise the library's choice for the shape. Returns a
  * negative status for arguments mhc_pre would reject. */
 MHC_API int mhc_pre_splits(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt);
 
@@ -95,10 +96,13 @@ MHC_API size_t mhc_pre_workspace_bytes(int64_t T, int n, int64_t D, int n_splits
  *   (pre, post, comb); bias float32 [N].
  * Knobs: sinkhorn_repeat >= 1; eps > 0; n_splits = split-K partials over the
  *   hidden axis: 0 = library choice; 1..256 = that many partials on the
- *   two-pass path; -1 = the single-pass path or an error (MHC_ERR_UNSUPPORTED
- *   for a shape it does not cover, MHC_ERR_MISALIGNED for an fn that is not
- *   16-byte aligned). Any value gives the same result up to fp32
- *   reassociation, and a fixed value is bitwise repeatable.
+ *   two-pass path; -1 = the single-pass path with the library's tiling, -S
+ *   (2 <= S <= 256) = the single-pass path with S slices of the hidden axis
+ *   (D = 32 * cps * S with cps one of 1, 2, 4, 5, 7, 8, 14), or an error for
+ *   either (MHC_ERR_UNSUPPORTED for a shape or slice count it does not cover,
+ *   MHC_ERR_MISALIGNED for an fn that is not 16-byte aligned); tile tables
+ *   and tuners choose among these values. Any value gives the same result
+ *   up to fp32 reassociation, and a fixed value is bitwise repeatable.
  * Paths: the single-pass kernel (one launch; the residual is read once and
  *   stays in registers; the workgroups of a token tile exchange partial sums
  *   through the workspace) covers bf16, n <= 4, D a multiple of 32 for which a

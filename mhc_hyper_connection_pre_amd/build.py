@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmhc.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["mhc_api.cpp", "mhc_pre.hip", "mhc_pre_resident.hip", "mhc_post.hip"]
+SOURCES = ["mhc_api.cpp", "mhc_tile_table.cpp", "mhc_pre.hip", "mhc_pre_resident.hip", "mhc_post.hip"]
 ARCH = os.environ.get("MHC_OFFLOAD_ARCH", "gfx950")
 
 COMMON_FLAGS = [

@@ -42,7 +42,11 @@ int check_shape(int64_t T, int n, int64_t D, mhc_dtype dt) {
 int make_pre_plan(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, PrePlan* p, bool boundary) {
   int st = check_shape(T, n, D, dt);
   if (st != MHC_OK) return st;
-  if (n_splits < kSplitsSinglePass || n_splits > 256) return MHC_ERR_INVALID_ARG;
+  if (n_splits < -kMaxSlices || n_splits > 256) return MHC_ERR_INVALID_ARG;
+  if (n_splits == 0 && T > 0) {
+    const int t = tuned_splits(T, n, D, dt, boundary);
+    if (t != 0 && make_pre_plan(T, n, D, t, dt, p, boundary) == MHC_OK) return MHC_OK;
+  }
   PrePlan q{};
   q.T = T;
   q.D = D;
@@ -92,11 +96,13 @@ int make_pre_plan(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, PrePl
   q.part_bytes = (size_t)q.S * (size_t)T * q.NP * sizeof(float);
   size_t total2 = align_up(q.off_part + q.part_bytes, 256);
   // Single-pass path: the library's choice when the shape allows it, or on
-  // request (n_splits = -1). Layout: status, packed fn (as above), then the
-  // tagged exchange words: partials [rS][T][N + 1] and pre [T][4], 8 bytes each.
+  // request (n_splits = -1, or -S for S slices). Layout: status, packed fn (as
+  // above), then the tagged exchange words: partials [rS][T][N + 1] and pre
+  // [T][4], 8 bytes each.
   ResidentChoice rc{};
-  const bool res_ok = n_splits <= 0 && resident_choose(T, n, D, dt, &rc, boundary);
-  if (n_splits == kSplitsSinglePass && !res_ok) return MHC_ERR_UNSUPPORTED;
+  const int want_S = n_splits < kSplitsSinglePass ? -n_splits : 0;
+  const bool res_ok = n_splits <= 0 && resident_choose(T, n, D, dt, &rc, boundary, want_S);
+  if (n_splits < 0 && !res_ok) return MHC_ERR_UNSUPPORTED;
   q.res = res_ok;
   q.total_bytes = total2;
   if (q.res) {
@@ -202,7 +208,7 @@ MHC_API int mhc_pre(float* post, float* comb, void* y, const void* residual, mhc
   if (!aligned(post, 4) || !aligned(comb, 4) || !aligned(fn, 4) || !aligned(hc_scale, 4) || !aligned(bias, 4))
     return MHC_ERR_MISALIGNED;
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.total_bytes) return MHC_ERR_WORKSPACE;
-  if (p.res && !aligned(fn, 16) && n_splits == kSplitsSinglePass) return MHC_ERR_MISALIGNED;
+  if (p.res && !aligned(fn, 16) && n_splits < 0) return MHC_ERR_MISALIGNED;
   return run_pre(p, post, comb, y, residual, fn, hc_scale, bias, sinkhorn_repeat, eps, workspace,
                  static_cast<hipStream_t>(stream));
 }
@@ -231,7 +237,7 @@ MHC_API int mhc_post_pre(void* out, float* post_next, float* comb_next, void* y_
     return MHC_ERR_MISALIGNED;
   const size_t need = fp.total_bytes > pp.total_bytes ? fp.total_bytes : pp.total_bytes;
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return MHC_ERR_WORKSPACE;
-  if (fp.res && !aligned(fn, 16) && n_splits == kSplitsSinglePass) return MHC_ERR_MISALIGNED;
+  if (fp.res && !aligned(fn, 16) && n_splits < 0) return MHC_ERR_MISALIGNED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (fp.res && aligned(fn, 16)) {
     const hipError_t er = launch_post_pre_resident(fp, h, residual, post, comb, out, fn, hc_scale, bias, post_next,

@@ -43,10 +43,18 @@ constexpr int kStMarker = 2;    // shape marker: the tag region was zeroed for t
 constexpr int kStDone = 16;     // finished workgroups of the running call (own 128-byte line)
 constexpr int kStArrive = 24;   // first-use barrier arrivals of the running call (own 128-byte line)
 
-// n_splits value that asks for the single-pass path.
+// n_splits value that asks for the single-pass path with the library's tiling;
+// n_splits = -S (2 <= S <= kMaxSlices) asks for it with S slices of the hidden
+// axis (a tile table or tuner picks among them).
 constexpr int kSplitsSinglePass = -1;
+constexpr int kMaxSlices = 256;
+
+// The tile table's n_splits for the shape (0 when no entry covers it).
+int tuned_splits(int64_t T, int n, int64_t D, mhc_dtype dt, bool boundary);
 
 // Fills `p`; returns MHC_OK or the status mhc_pre would return for the sizes.
+// n_splits = 0 takes the tile table's entry when one covers the shape and is
+// valid for it, and the heuristic below otherwise.
 // boundary: plan the layer-boundary call (mhc_post_pre), whose single-pass
 // kernel also keeps the block output in registers.
 int make_pre_plan(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, PrePlan* p, bool boundary = false);
@@ -68,11 +76,13 @@ hipError_t launch_post_pre_resident(const PrePlan& p, const void* h, const void*
                                     const float* bias, float* post, float* comb, void* y, void* workspace,
                                     int repeat, float eps, hipStream_t s);
 // Single-pass tiling for the shape on the current device (or a 256-CU MI355X
-// when no device is visible): false if the shape is not supported.
+// when no device is visible): false if the shape is not supported. want_S > 0
+// restricts the choice to that many slices of the hidden axis.
 struct ResidentChoice {
   int cps, S, per, TB;
 };
-bool resident_choose(int64_t T, int n, int64_t D, mhc_dtype dt, ResidentChoice* c, bool boundary = false);
+bool resident_choose(int64_t T, int n, int64_t D, mhc_dtype dt, ResidentChoice* c, bool boundary = false,
+                     int want_S = 0);
 constexpr int kResidentTile = 128;
 
 hipError_t launch_post(const void* h, const void* residual, const float* post, const float* comb,

@@ -611,18 +611,35 @@ struct OccQuery {
   int operator()() const { return occupancy_of<NS, CPS, POST>(); }
 };
 
+template <bool POST>
+struct FitsQuery {
+  template <int NS, int CPS>
+  int operator()() const { return (POST ? ResShape<NS, CPS>::fits_post : ResShape<NS, CPS>::fits) ? 1 : 0; }
+};
+
+// Workgroups per CU without a device to ask: 0 for a tiling that is not
+// built, else from the kernels' register counts (more than 128 VGPRs, one
+// workgroup per CU, except the narrowest tilings).
+int static_occupancy(int n, int cps, bool post) {
+  const int fits = post ? dispatch(n, cps, FitsQuery<true>{}) : dispatch(n, cps, FitsQuery<false>{});
+  if (!fits) return 0;
+  const int regs = 4 * n * cps + (post ? 4 * cps : 0);
+  return regs > 8 ? 1 : 2;
+}
+
 // Workgroups per CU for (n, cps, layer boundary or not) on the current
-// device, cached; -1 when no device answers (then a static estimate is used).
+// device, cached; the static estimate when no device answers.
 int occupancy(int n, int cps, bool post) {
   constexpr int kMaxDev = 64;
   static std::atomic<int> cache[kMaxDev][2][5][16];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipGetDevice(&dev) != hipSuccess) return static_occupancy(n, cps, post);
   if (dev < kMaxDev) {
     const int c = cache[dev][post][n][cps].load(std::memory_order_acquire);
     if (c != 0) return c - 2;
   }
-  const int occ = post ? dispatch(n, cps, OccQuery<true>{}) : dispatch(n, cps, OccQuery<false>{});
+  int occ = post ? dispatch(n, cps, OccQuery<true>{}) : dispatch(n, cps, OccQuery<false>{});
+  if (occ < 0) occ = static_occupancy(n, cps, post);   // the runtime could not answer
   if (dev < kMaxDev) cache[dev][post][n][cps].store(occ + 2, std::memory_order_release);
   return occ;
 }
@@ -636,7 +653,7 @@ int device_cus() {
 
 }  // namespace
 
-bool resident_choose(int64_t T, int n, int64_t D, mhc_dtype dt, ResidentChoice* out, bool post) {
+bool resident_choose(int64_t T, int n, int64_t D, mhc_dtype dt, ResidentChoice* out, bool post, int want_S) {
   if (dt != MHC_BF16 || T <= 0 || n < 1 || n > 4 || D % 32 != 0) return false;
   if ((int64_t)kTM * n * D >= (1LL << 31)) return false;   // 32-bit lane offsets within a tile
   const int tiles = (int)((T + kTM - 1) / kTM);
@@ -648,10 +665,9 @@ bool resident_choose(int64_t T, int n, int64_t D, mhc_dtype dt, ResidentChoice* 
     const int regs = 4 * n * cps + (post ? 4 * cps : 0);   // residual (+ block output) registers
     if (D % (32 * cps) != 0 || regs > (post ? kMaxAVgprsPost : kMaxAVgprs)) continue;
     const int64_t S = D / (32 * cps);
-    if (S > kMaxSplits) continue;
+    if (S > kMaxSplits || (want_S > 0 && S != want_S)) continue;
     if ((double)S * (double)T * (n * (n + 2) + 1) * 8.0 >= 2147483648.0) continue;   // 32-bit exchange offsets
-    int occ = occupancy(n, cps, post);
-    if (occ < 0) occ = regs > 96 ? 1 : 2;   // no device: static estimate
+    const int occ = occupancy(n, cps, post);
     const int64_t cap = (int64_t)occ * cus;
     if (cap < S) continue;
     int per = (int)(cap / S);

@@ -76,8 +76,9 @@ def test_pre_validation(L):
     assert pre(L, repeat=0) == INVALID
     assert pre(L, eps=0.0) == INVALID
     assert pre(L, eps=float("nan")) == INVALID
-    assert pre(L, splits=-2) == INVALID
+    assert pre(L, splits=-257) == INVALID
     assert pre(L, splits=257) == INVALID
+    assert pre(L, splits=-3) == UNSUPPORTED        # 3 slices do not divide D = 64 into 32-wide steps
     for k in ("post", "comb", "y", "res", "fn", "hc", "bias"):
         assert pre(L, **{k: None}) == INVALID, k
     assert pre(L, y=A + 8) == MISALIGNED
@@ -118,7 +119,15 @@ def test_pre_plan(L):
     assert L.mhc_pre_splits(T, n, 104, -1, BF16) == UNSUPPORTED        # D % 32 != 0
     assert L.mhc_pre_splits(T, n, 104, 0, BF16) >= 1                    # ... two-pass instead
     assert L.mhc_pre_splits(8, 4, 256, -1, F32) == UNSUPPORTED           # fp32: two-pass only
-    assert L.mhc_pre_splits(T, n, D, -2, BF16) == INVALID
+    assert L.mhc_pre_splits(T, n, D, -257, BF16) == INVALID
+    # explicit single-pass slice counts: D = 32 * cps * S for a built cps, else unsupported
+    for S_ in (32, 56, 112):
+        assert L.mhc_pre_splits(T, n, D, -S_, BF16) == S_
+        assert L.mhc_pre_workspace_bytes(T, n, D, -S_, BF16) == 256 + fnp + (S_ * T * 25 * 8 + 255) // 256 * 256 + T * 4 * 8
+    assert L.mhc_pre_splits(T, n, D, -16, BF16) == UNSUPPORTED       # cps 14: its residual slice needs too many registers
+    assert L.mhc_pre_splits(T, n, D, -28, BF16) == UNSUPPORTED       # cps 8: its fn fragments do not fit in LDS
+    assert L.mhc_pre_splits(T, n, D, -2, BF16) == UNSUPPORTED        # cps 112 is not built
+    assert L.mhc_pre_splits(T, n, 104, -1, F32) == UNSUPPORTED
     # fp32 residuals always take the two-pass path (no packed fn)
     assert L.mhc_pre_workspace_bytes(8, 4, 256, 0, F32) == 256 + (L.mhc_pre_splits(8, 4, 256, 0, F32) * 8 * 28 * 4 + 255) // 256 * 256
     # n = 8 (N = 80): two-pass only; [hi | lo | lo2 of the 8 pre columns] = 168 -> 11 blocks; partials [S, T, 84]
@@ -156,7 +165,8 @@ def test_post_pre_validation(L):
     assert pp(D=12) == MISALIGNED
     assert pp(R=0) == INVALID
     assert pp(eps=0.0) == INVALID
-    assert pp(sp=-2) == INVALID
+    assert pp(sp=-257) == INVALID
+    assert pp(sp=-3) == UNSUPPORTED              # no single-pass tiling with 3 slices of D = 64
     assert pp(dt=F32, sp=-1) == UNSUPPORTED      # the single-pass kernel is bf16 only
     assert pp(h=None) == INVALID
     assert pp(fn=None) == INVALID
