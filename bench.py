@@ -143,7 +143,7 @@ def write_traffic(fetch_dir, write_dir, command):
         total = f_kib * 1024 * fs + w_kib * 1024 * ws
         with open(os.path.join(PROFILES, fname), "w") as f:
             f.write(f"# HBM traffic of {k}, prefill T=2048 n=4 D=7168 bf16, per launch\n")
-            f.write("# two rocprofv3 counter passes (one counter each), from the repository root on the MI355X box:\n")
+            f.write("# two rocprofv3 counter passes (one counter each), from the repository root on an MI355X:\n")
             for line in command:
                 f.write(f"#   {line}\n")
             f.write(f"# calibration: the 1 GiB copy reads FETCH_SIZE {max(fetch[copy[0]]):.0f} KiB and WRITE_SIZE "
