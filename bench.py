@@ -35,6 +35,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -86,11 +87,23 @@ def pcn_bytes(T, n, D, e):
 
 # ---------------------------------------------------------------- traffic from counters
 
-def source_hash(which):
+def code_text(src: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed: edits to comments keep the hash."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
+def source_hash(which, read=None):
+    """Hash of the code (comments excluded) of the sources a traffic profile depends on."""
     h = hashlib.sha256()
     for name in TRAFFIC[which][2]:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        if read is None:
+            with open(os.path.join(CSRC, name)) as f:
+                text = f.read()
+        else:
+            text = read(name)
+        h.update(code_text(text).encode())
     return h.hexdigest()[:16]
 
 
@@ -151,7 +164,7 @@ def write_traffic(fetch_dir, write_dir, command):
             f.write(f"# {len(fetch[k])} dispatches: FETCH_SIZE {f_kib:.1f} KiB = {f_kib * 1024 * fs / 1e6:.1f} MB read, "
                     f"WRITE_SIZE {w_kib:.1f} KiB = {w_kib * 1024 * ws / 1e6:.1f} MB written\n")
             f.write(f"# algorithmic bytes per launch: {algo[which]} ({algo[which] / 1e6:.1f} MB)\n")
-            f.write(f"# sources: {', '.join(sources)}\n")
+            f.write(f"# sources: {', '.join(sources)} (the hash covers their code, comments excluded)\n")
             f.write(f"kernel_source_sha256_16: {source_hash(which)}\n")
             f.write(f"fetch_scale: {fs:.5f}\nwrite_scale: {ws:.5f}\n")
             f.write(f"hbm_bytes_per_launch: {total:.0f}\n")

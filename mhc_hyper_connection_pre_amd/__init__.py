@@ -141,7 +141,11 @@ def mhc_pre_sync_timeouts(workspace, residual, n_splits: int = 0, stream=None) -
 
 def mhc_pre(residual, fn, hc_scale, bias, *, sinkhorn_repeat: int = 20, eps: float = 1e-6, n_splits: int = 0,
             post=None, comb=None, y=None, workspace=None, stream=None):
-    """post [T, n] f32, comb [T, n, n] f32, y [T, D] = mhc_pre(residual [T, n, D], fn, hc_scale, bias)."""
+    """post [T, n] f32, comb [T, n, n] f32, y [T, D] = mhc_pre(residual [T, n, D], fn, hc_scale, bias).
+
+    n_splits as in ``include/mhc.h``: 0 = the library's tiling (its tile table, else a heuristic), S > 0 = the
+    two-pass path with S split-K partials, -1 = the single-pass kernel, -S = the single-pass kernel with S slices.
+    """
     torch = _torch()
     L = lib()
     T, n, D = residual.shape

@@ -15,10 +15,11 @@
 // (a 128-token tile) x all n streams x hidden positions [DS s, DS s + DS),
 // DS = 32 CPS. Wave w keeps its 16 tokens x n x DS positions as MFMA A
 // fragments (4 n CPS VGPRs: 112 at n = 4, CPS = 7). The grid holds P = G x S
-// workgroups, all resident at once (the host sizes G by the occupancy);
-// workgroup b always takes slice s = b % S and tiles b / S, + G, + 2G, ...
-// ("generations": two of 1024 tokens at T = 2048, n = 4, D = 7168). Per
-// workgroup:
+// workgroups, all resident at once (the host sizes G by the occupancy); a
+// workgroup keeps one slice s and takes tiles t, t + G, t + 2G, ...
+// ("generations": two of 1024 tokens at T = 2048, n = 4, D = 7168; the
+// workgroup -> (t, s) mapping gives each XCD runs of neighbouring slices).
+// Per workgroup:
 //   0. once: its slice of fn is loaded (fp32), split into bf16 terms (hi, lo,
 //      and lo2 for the pre columns), packed into MFMA B fragments and kept in
 //      LDS; the first residual loads follow it
