@@ -14,7 +14,8 @@ ms_per_step); the same K steps then run again with a HIP event on the launch
 stream around every call (events without the system-scope fence), which gives
 each kernel's average duration. A third pass times the layer boundary as one
 call, mhc_post_pre (post of one layer, then the next layer's pre), on the same
-buffers ("boundary").
+buffers ("boundary"); at decode sizes also with sixteen boundary calls captured
+in one HIP graph ("graph_of_16_us_per_call").
 
 Prints one JSON line: tokens/s (value), algorithmic HBM GB/s and its fraction
 of the 8 TB/s peak, a roofline object for the dominant kernel (algorithmic
@@ -422,6 +423,29 @@ def run(args):
                 "us_per_call": us_b, "tokens_per_s": T / (us_b * 1e-6), "algorithmic_bytes": bb,
                 "gbps": bb / (us_b * 1e-6) / 1e9, "frac_of_peak": bb / (us_b * 1e-6) / 1e9 / PEAK_HBM_GBPS,
                 "vs_pre_plus_post_step": ms_per_step * 1e3 / us_b}
+
+    # Decode sizes: the layer boundaries of a 16-layer stretch captured in one
+    # HIP graph (a decode step's launches as one replay), per boundary call.
+    if one and T <= 256 and not args.graph:
+        layers = 16
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for i in range(layers):
+                b = sets[i % nsets]
+                mhc.mhc_post_pre(b["h"], b["residual"], b["post"], b["comb"], fn, hc, bias,
+                                 sinkhorn_repeat=spec.sinkhorn_repeat, eps=spec.eps, n_splits=spec.n_splits,
+                                 out=b["out"], post_next=b["post_next"], comb_next=b["comb_next"], y=b["y"],
+                                 workspace=ws, stream=torch.cuda.current_stream(dev))
+        for _ in range(3):
+            gr.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // layers)
+        t4 = time.perf_counter()
+        for _ in range(reps):
+            gr.replay()
+        torch.cuda.synchronize()
+        boundary["graph_of_16_us_per_call"] = (time.perf_counter() - t4) * 1e6 / (reps * layers)
+        del gr
 
     # practical ceiling: a 1 GiB device-to-device copy kernel on the same stream
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
