@@ -226,6 +226,46 @@ def test_boundary_graph_replay():
         torch.cuda.synchronize()
 
 
+def test_boundary_layers_in_one_graph():
+    """Decode size: eight boundary calls (a chain of layers: each call's out is the next call's residual) captured
+    in one graph on one workspace, replayed three times with an eager call in between; every layer's outputs equal
+    the same chain run eagerly, bit for bit."""
+    T, n, D, L = 64, 4, 5120, 8
+    assert mhc.mhc_post_pre_fused(T, n, D, 0, 0)
+    x = W.generate(W.custom(T, n, D, "bf16", seed=77, fn_std=0.02))
+    g, post, comb, fn2 = _case(x)
+    s = x.spec
+    ws = _workspace(s, 0)
+    outs = [[torch.empty_like(g["residual"]), torch.empty_like(g["post_in"]), torch.empty_like(g["comb_in"]),
+             torch.empty_like(g["h"])] for _ in range(L)]
+
+    def chain(stream):
+        res, p, c = g["residual"], g["post_in"], g["comb_in"]
+        for o in outs:
+            mhc.mhc_post_pre(g["h"], res, p, c, g["fn2"], g["hc_scale"], g["bias"], sinkhorn_repeat=s.sinkhorn_repeat,
+                             eps=s.eps, out=o[0], post_next=o[1], comb_next=o[2], y=o[3], workspace=ws,
+                             stream=stream)
+            res, p, c = o[0], o[1], o[2]
+
+    chain(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    eager = [[t.clone() for t in o] for o in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        chain(torch.cuda.current_stream())
+    for k in range(3):
+        for o in outs:
+            for t in o:
+                t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for li, (o, e) in enumerate(zip(outs, eager)):
+            for t, te in zip(o, e):
+                assert torch.equal(t, te), f"replay {k}, layer {li} differs from the eager chain"
+        _boundary(x, g, 0, ws)   # an eager call on the same workspace between replays
+        torch.cuda.synchronize()
+
+
 def test_boundary_errors():
     x = W.generate(W.custom(8, 4, 512, "bf16", seed=7))
     g, _, _, _ = _case(x)
