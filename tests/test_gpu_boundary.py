@@ -101,7 +101,8 @@ def _check_oracle(x, outs, post, comb, fn2, what, tokens=None):
 
 
 FUSED = [(1, 4, 512), (31, 4, 1024), (67, 3, 1024), (130, 2, 512), (17, 1, 2048), (64, 4, 5120),
-         (129, 4, 1056), (300, 3, 2240), (1100, 4, 7168)]   # the last: two generations, the second ragged
+         (129, 4, 1056), (300, 3, 2240), (1100, 4, 7168),   # two generations, the second ragged
+         (700, 4, 2560), (1500, 3, 6144)]
 FALLBACK = [(7, 4, 264, "bf16"), (33, 4, 1032, "f32"), (5, 2, 72, "bf16"), (9, 8, 1032, "bf16"),
             (5, 8, 256, "f32")]
 

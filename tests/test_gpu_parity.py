@@ -91,7 +91,8 @@ def test_small_pre_post(T, n, D, dt, sp):
 # single-pass path: bf16 with D a multiple of 128 (tiles of 128 tokens, slices of 128)
 SINGLE_PASS = [(1, 4, 512), (31, 4, 1024), (33, 4, 1536), (67, 3, 1024), (130, 2, 512), (17, 1, 2048), (64, 4, 5120),
          (100, 4, 7168), (5, 4, 16384), (129, 4, 1056), (300, 3, 2240), (257, 2, 448),
-         (1100, 4, 7168)]   # the last: two generations of tiles, the second one ragged
+         (1100, 4, 7168),   # two generations of tiles, the second one ragged
+         (700, 4, 2560), (2048, 4, 6144), (1500, 3, 6144)]   # slice counts 40, 48, 24 (XCD slice runs of 5, 6, 3)
 
 
 @pytest.mark.parametrize("T,n,D", SINGLE_PASS, ids=lambda v: str(v))
