@@ -129,7 +129,10 @@ struct ResShape {
   static constexpr int KSW = NS * CPS;            // k-steps of a slice
   static constexpr int PER_STREAM = CPS * NCB;    // 1 KB fragment blocks per stream
   static constexpr int BBLK = NS * PER_STREAM;     // the slice's B fragments
-  static constexpr int kRed = kWaves * 16 * CW;   // per-wave partial rows
+  // per wave: its 16 partial rows, later two staging buffers for output
+  // stores (16 rows x 144 bytes each: 128 of data and 16 of padding)
+  static constexpr int kWaveScratch = 16 * CW > 2 * 16 * 36 ? 16 * CW : 2 * 16 * 36;
+  static constexpr int kRed = kWaves * kWaveScratch;
   static constexpr int kGs = 16 * 32;             // finalise group sums
   static constexpr int kScratch = kRed + kGs;      // per-wave partial rows, then the group sums
   static constexpr size_t lds_bytes = (size_t)BBLK * 1024 + (size_t)kScratch * 4;   // B, then the scratch
@@ -250,6 +253,53 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
     }
   };
 
+  // Output stores. A lane holds 16 bytes (8 values) of one row of a 32-wide
+  // column: row r16, bytes 16 q .. 16 q + 15 of the column. Streaming stores
+  // of such 16-row x 64-byte pieces write partial 128-byte lines (a 117 MB
+  // tensor in this pattern: 17 % more bytes written and 38 % more time than
+  // whole lines). So the slice's columns are stored in units that cover whole
+  // lines: with phase p = 1 when the slice's first column starts in the middle
+  // of a line, unit u is columns (2u - p, 2u + 1 - p), a column outside the
+  // slice being absent. Each column goes into its unit's half of a staging
+  // buffer in LDS as soon as it is formed (two buffers per wave, used by
+  // alternate units), and a complete unit goes out as two 8-row x 128-byte
+  // stores. The phase only moves LDS addresses and lane masks, so every wave
+  // issues the same instruction sequence. Rows and streams start on lines
+  // when D is a multiple of 64 (and the tensors are 128-byte aligned);
+  // otherwise some rows or streams straddle lines, which costs bandwidth, not
+  // correctness.
+  // With at most two columns per slice (decode tilings) a unit is at most one
+  // line per row and the staging's LDS round trips cost more latency than the
+  // partial lines cost bandwidth: such slices store column by column.
+  constexpr bool kUnitStores = CPS >= 4;
+  constexpr int kUnits = CPS / 2 + 1;   // units that can hold a column of the slice
+  u32x4* stage = reinterpret_cast<u32x4*>(scratch + w * F::kWaveScratch);   // 2 x 16 rows x 144 bytes
+  // column c of the slice into its unit's half of buffer (slot + unit) & 1
+  auto stage_col = [&](int slot, int phase, int c, const u32x4& v) {
+    const int uc = c + phase;
+    stage[((slot + (uc >> 1)) & 1) * 144 + r16 * 9 + (uc & 1) * 4 + q] = v;
+  };
+  // unit u from buffer (slot + u) & 1 to memory. col0: element pointer of this
+  // wave's first row at the slice's column 0 (uniform); off: this lane's
+  // element offsets for its rows h * 8 + lane / 8 (h = 0, 1) and its 16 bytes
+  // lane % 8 of a line; rows: the wave's rows below T.
+  auto flush_unit = [&](int slot, int phase, int u, uint16_t* col0, const uint32_t (&off)[2], int rows) {
+    const int c0 = 2 * u - phase;   // the unit's first column (-1 or CPS: absent)
+    const bool lo_in = c0 >= 0 && c0 < CPS, hi_in = c0 + 1 < CPS;
+    const u32x4* buf = stage + ((slot + u) & 1) * 144;
+    uint16_t* base = col0 + c0 * 32;   // uniform; only lanes of present columns store
+    wait_lgkm();   // the reads below take what other lanes of this wave wrote
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = h * 8 + (lane >> 3), k = lane & 7;
+      const u32x4 v = buf[r * 9 + k];
+      if (r < rows && (k < 4 ? lo_in : hi_in)) st16_stream(base + off[h], v);
+    }
+  };
+  // a unit is complete once column min(2u + 1, CPS - 1) is staged
+  auto unit_done = [](int u) { return 2 * u + 1 < CPS ? 2 * u + 1 : CPS - 1; };
+
   // ---- 0. fn slice -> B fragments in LDS (once). Fragment
   // ((i CPS + kk) NCB + cb) 64 + l holds B[k][col] for k = 32 kk + 8 (l / 16)
   // + e of stream i's slice (fn row i D + d0 + k) and col = 16 cb + l % 16:
@@ -325,7 +375,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
     const int64_t row = (int64_t)tile * kTM + w * 16 + r16;
     const bool rok = row < T;
 
-    // layer boundary: where this lane's out values go
+    // layer boundary: the tile's out slice (and this lane's offset in it)
     uint16_t* ob = nullptr;
     uint32_t oo = 0;
     if constexpr (POST) {
@@ -391,7 +441,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
     // wave's rows are consecutive tokens, so its 16 (N + 1) words are
     // contiguous in the exchange buffer: lane l writes words l, l + 64, ...,
     // and each store instruction covers one contiguous run.
-    float* rw = scratch + w * (16 * CW);
+    float* rw = scratch + w * F::kWaveScratch;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -419,7 +469,24 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
     // layer boundary: out goes to HBM now, while the tile's exchange below
     // leaves HBM mostly idle (stored during the GEMM it competed with the
     // residual loads: 8 us more per call at T = 2048, n = 4, D = 7168)
-    if constexpr (POST) {
+    if constexpr (POST && kUnitStores) {
+      const int64_t wrow0 = (int64_t)tile * kTM + w * 16;
+      const int wrows = T - wrow0 < 16 ? (int)(T - wrow0) : 16;
+      uint16_t* obw = ob + (uint32_t)(w * 16 * NS * (int)D);
+      const uint32_t off[2] = {(uint32_t)((lane >> 3) * NS * (int)D + (lane & 7) * 8),
+                               (uint32_t)((8 + (lane >> 3)) * NS * (int)D + (lane & 7) * 8)};
+      const int phase = (int)(d0 >> 5) & 1;   // as every stream when D is a multiple of 64
+#pragma unroll
+      for (int jj = 0; jj < NS; ++jj) {
+#pragma unroll
+        for (int c = 0; c < CPS; ++c) {
+          stage_col(jj * kUnits, phase, c, A[jj * CPS + c]);
+#pragma unroll
+          for (int u = 0; u < kUnits; ++u)
+            if (c == unit_done(u)) flush_unit(jj * kUnits, phase, u, obw + jj * D, off, wrows);
+        }
+      }
+    } else if constexpr (POST) {
 #pragma unroll
       for (int c = 0; c < CPS; ++c)
 #pragma unroll
@@ -532,9 +599,14 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
     // tile's residual right after, so those loads overlap the rest of y
     {
       uint16_t* yb = a.y + (int64_t)tile * kTM * D + d0;
-      const uint32_t yo = (uint32_t)((w * 16 + r16) * (int)D + q * 8);
       const int nlr = lane_row(tile + G);
       if constexpr (NEXT) load_pw(tile + G);
+      const int64_t wrow0 = (int64_t)tile * kTM + w * 16;
+      const int wrows = T - wrow0 < 16 ? (int)(T - wrow0) : 16;
+      uint16_t* ybw = yb + (uint32_t)(w * 16 * (int)D);
+      const int phase = (int)(d0 >> 5) & 1;
+      const uint32_t off[2] = {(uint32_t)((lane >> 3) * (int)D + (lane & 7) * 8),
+                               (uint32_t)((8 + (lane >> 3)) * (int)D + (lane & 7) * 8)};
 #pragma unroll
       for (int c = 0; c < CPS; ++c) {
         float o[8], f[8];
@@ -547,8 +619,16 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
 #pragma unroll
           for (int v = 0; v < 8; ++v) o[v] = fmaf(pre[i], f[v], o[v]);
         }
-        if (rok) st16_stream(yb + yo + c * 32, Vec<BF16>::pack(o));
-        if constexpr (NEXT) load_col(tile + G, nlr, c);
+        if constexpr (kUnitStores) {
+          stage_col(0, phase, c, Vec<BF16>::pack(o));
+          if constexpr (NEXT) load_col(tile + G, nlr, c);
+#pragma unroll
+          for (int u = 0; u < kUnits; ++u)
+            if (c == unit_done(u)) flush_unit(0, phase, u, ybw, off, wrows);
+        } else {
+          if (rok) st16_stream(yb + (uint32_t)((w * 16 + r16) * (int)D + q * 8) + c * 32, Vec<BF16>::pack(o));
+          if constexpr (NEXT) load_col(tile + G, nlr, c);
+        }
       }
     }
   };
