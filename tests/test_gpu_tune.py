@@ -30,7 +30,9 @@ def _ws(T, n, D, n_splits):
 
 
 @pytest.mark.parametrize("T,n,D,S", [(300, 4, 7168, 32), (300, 4, 7168, 56), (300, 4, 7168, 112),
-                                     (64, 4, 5120, 32), (64, 4, 5120, 40), (129, 2, 2048, 16)])
+                                     (64, 4, 5120, 32), (64, 4, 5120, 40), (129, 2, 2048, 16),
+                                     # D not a multiple of 64: rows and slices start mid-line (line-unit stores)
+                                     (300, 4, 1120, 5), (300, 4, 1120, 7), (200, 3, 2016, 9)])
 def test_explicit_single_pass_tiling(T, n, D, S):
     assert mhc.mhc_pre_splits(T, n, D, -S, 0) == S
     x, g = _inputs(T, n, D, seed=T + S)
@@ -46,9 +48,8 @@ def test_explicit_single_pass_tiling(T, n, D, S):
     assert_close(host(y), oy, "tensor", f"S={S} y")
 
 
-@pytest.mark.parametrize("S", [32, 56])
-def test_boundary_explicit_tiling_matches_its_two_calls(S):
-    T, n, D = 200, 4, 7168
+@pytest.mark.parametrize("T,n,D,S", [(200, 4, 7168, 32), (200, 4, 7168, 56), (150, 4, 1120, 7), (257, 2, 1120, 5)])
+def test_boundary_explicit_tiling_matches_its_two_calls(T, n, D, S):
     assert mhc.mhc_post_pre_fused(T, n, D, -S, 0)
     x, g = _inputs(T, n, D, seed=S)
     post_in = torch.rand((T, n), device="cuda", generator=torch.Generator(device="cuda").manual_seed(1))
