@@ -191,9 +191,9 @@ def pin_sinkhorn_exact(O):
 
 def pin_sinkhorn_closed_forms(O):
     """Constant logits -> J/n; diagonal a / off-diagonal b -> closed form; n = 2 limit."""
-    for n in (1, 2, 3, 4, 5):
+    for n in (1, 2, 3, 4, 5, 8):
         _close(O.sinkhorn(np.full((1, n, n), 0.7), 20)[0], np.full((n, n), 1.0 / n), rtol=1e-15)
-    for n, a, b in ((3, 1.0, -0.5), (4, -2.0, 0.3)):
+    for n, a, b in ((3, 1.0, -0.5), (4, -2.0, 0.3), (8, 0.4, -1.1)):
         Z = np.full((1, n, n), b)
         Z[0][np.diag_indices(n)] = a
         den = math.exp(a) + (n - 1) * math.exp(b)
