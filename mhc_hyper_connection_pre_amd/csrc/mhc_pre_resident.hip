@@ -160,7 +160,8 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
   float* scratch = reinterpret_cast<float*>(lds + F::BBLK * 64);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  // the wave index is uniform: in a scalar register, so are the per-wave bases
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, q = lane >> 4;
   const int S = a.S, G = a.G;
   // Workgroup -> (tile slot, slice). Workgroups are dispatched to the eight
@@ -301,10 +302,15 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
   auto unit_done = [](int u) { return 2 * u + 1 < CPS ? 2 * u + 1 : CPS - 1; };
 
   // ---- 0. fn slice -> B fragments in LDS (once). Fragment
-  // ((i CPS + kk) NCB + cb) 64 + l holds B[k][col] for k = 32 kk + 8 (l / 16)
+  // ((kk NS + i) NCB + cb) 64 + l holds B[k][col] for k = 32 kk + 8 (l / 16)
   // + e of stream i's slice (fn row i D + d0 + k) and col = 16 cb + l % 16:
   // hi = bf16(f) in columns < N, lo = bf16(f - hi) in N .. 2N - 1, lo2 =
   // bf16(f - hi - lo) of the n pre columns next, zero beyond (mhc_pack.h).
+  // Fragments follow the GEMM's k-step order (column kk of every stream, then
+  // column kk + 1), so the reads of one column lie in one run of LDS and a
+  // few base registers with immediate offsets reach all of them (stream-major
+  // order made the compiler keep a base per column, and spill at the layer
+  // boundary, where a reload waits for every residual load in flight).
   // Each packing unit loads its 8 fn rows x VW columns straight into
   // registers and writes the VW columns' hi, lo (and lo2) fragments.
   {
@@ -315,7 +321,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
       const int u0 = tid + uu * kThreads;
       const int u = u0 < F::PU ? u0 : F::PU - 1;   // no branch: the waits stay exact
       const int g = u % F::NG, jq = u / F::NG;
-      const int j = jq >> 2, i = j / CPS, kk = j - i * CPS;
+      const int j = jq >> 2, kk = j / NS, i = j - kk * NS;
       const float* src = a.fn + ((int64_t)i * D + d0 + kk * 32 + (jq & 3) * 8) * N + g * F::VW;
 #pragma unroll
       for (int e = 0; e < 8; ++e) fv[uu][e] = *reinterpret_cast<const FV*>(src + e * N);
@@ -426,7 +432,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
           acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              av, __builtin_bit_cast(bf16x8, Bl[(j * NCB + cb) * 64 + lane]), acc[cb], 0, 0, 0);
+              av, __builtin_bit_cast(bf16x8, Bl[((c * NS + i) * NCB + cb) * 64 + lane]), acc[cb], 0, 0, 0);
         ss = dot2_self(aw.x, ss);
         ss = dot2_self(aw.y, ss);
         ss = dot2_self(aw.z, ss);
