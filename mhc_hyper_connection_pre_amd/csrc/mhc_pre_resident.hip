@@ -160,8 +160,12 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
   float* scratch = reinterpret_cast<float*>(lds + F::BBLK * 64);
 
   const int tid = threadIdx.x;
-  // the wave index is uniform: in a scalar register, so are the per-wave bases
-  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // The wave index is uniform. At the layer boundary it is read into a scalar
+  // register, so the per-wave bases are scalar too (VGPRs are what that
+  // instantiation runs out of); the pre instantiations measured 0.3-0.7 us
+  // slower that way at T = 32, D = 5120 and no faster at T = 2048, so they
+  // keep it in a vector register.
+  const int lane = tid & 63, w = POST ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int r16 = lane & 15, q = lane >> 4;
   const int S = a.S, G = a.G;
   // Workgroup -> (tile slot, slice). Workgroups are dispatched to the eight
