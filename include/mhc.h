@@ -91,6 +91,8 @@ MHC_API size_t mhc_pre_workspace_bytes(int64_t T, int n, int64_t D, int n_splits
  * Outputs (first, in the order the page's call returns them):
  *   post  float32 [T, n]        comb float32 [T, n, n] (comb[t][i][j]: stream i -> j)
  *   y     dt      [T, D]
+ *   They must not overlap one another, an input or the workspace bytes the
+ *   call uses (MHC_ERR_INVALID_ARG).
  * Inputs:
  *   residual dt [T, n, D]; fn float32 [n*D, N]; hc_scale float32 [3]
  *   (pre, post, comb); bias float32 [N].
@@ -140,7 +142,7 @@ MHC_API int mhc_pre_sync_timeouts(const void* workspace, size_t workspace_bytes,
  * mhc_post - [P1] section 2 (the post call, into a tensor shaped like the
  * residual):
  *   out[t][j][d] = post[t][j] * h[t][d] + sum_i comb[t][i][j] * residual[t][i][d]
- * Output: out dt [T, n, D] (may not alias the inputs).
+ * Output: out dt [T, n, D] (must not overlap an input: MHC_ERR_INVALID_ARG).
  * Inputs: h dt [T, D] (the block output); residual dt [T, n, D];
  *   post float32 [T, n]; comb float32 [T, n, n] as mhc_pre writes them.
  */
@@ -159,9 +161,9 @@ MHC_API int mhc_post(void* out, const void* h, const void* residual,
  *   post_next, comb_next, y_next = mhc_pre(out, fn, hc_scale, bias, ...)
  * exactly as the two calls in sequence (the same bits as mhc_post followed by
  * mhc_pre with the same knobs, when both run the same pre path).
- * Outputs: out dt [T, n, D] (must not overlap residual or h: else
- *   MHC_ERR_INVALID_ARG); post_next float32 [T, n]; comb_next float32
- *   [T, n, n]; y_next dt [T, D].
+ * Outputs: out dt [T, n, D]; post_next float32 [T, n]; comb_next float32
+ *   [T, n, n]; y_next dt [T, D]. They must not overlap one another, an
+ *   input or the workspace bytes the call uses (MHC_ERR_INVALID_ARG).
  * Inputs: h, residual, post, comb as mhc_post (post and comb of the finished
  *   layer); fn, hc_scale, bias of the next layer as mhc_pre.
  * Knobs, workspace and errors: as mhc_pre (same workspace size and status
@@ -190,7 +192,8 @@ MHC_API int mhc_post_pre_fused(int64_t T, int n, int64_t D, int n_splits, mhc_dt
  *   c[d]          = sum_j combine_w[t][j] * o_j[d], rounded to dt
  *   normalized[d] = (c[d] / sqrt(sum_d c[d]^2 / D + norm_eps)) * norm_weight[d], rounded to dt
  * Outputs: normalized dt [T, D]; out_residual dt [T, n, D] receives o (pass
- *   NULL to skip writing it).
+ *   NULL to skip writing it). They must not overlap each other or an input
+ *   (MHC_ERR_INVALID_ARG).
  * Inputs: as mhc_post, plus combine_w float32 [T, n] and norm_weight float32
  *   [D]; norm_eps > 0. D <= 32768 (bf16) or 16384 (f32).
  */

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <initializer_list>
 #include <cstdio>
 
 #include "mhc_internal.h"
@@ -153,6 +154,29 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// A buffer an entry point touches: its address and the bytes the call reads
+// or writes there (null: an optional buffer that is absent).
+struct Span {
+  const void* p;
+  size_t bytes;
+};
+
+// True when a written buffer overlaps another written buffer or a read one.
+// The kernels read inputs and write outputs from many workgroups in no fixed
+// order, so such an overlap would make the results depend on the schedule.
+bool outputs_overlap(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+  for (auto o = outs.begin(); o != outs.end(); ++o) {
+    if (!o->p) continue;
+    for (auto q = o + 1; q != outs.end(); ++q)
+      if (q->p && overlaps(o->p, o->bytes, q->p, q->bytes)) return true;
+    for (const Span& i : ins)
+      if (i.p && overlaps(o->p, o->bytes, i.p, i.bytes)) return true;
+  }
+  return false;
+}
+
+size_t elem_bytes(mhc_dtype dt) { return dt == MHC_BF16 ? 2 : 4; }
+
 }  // namespace
 
 }  // namespace mhc
@@ -209,6 +233,14 @@ MHC_API int mhc_pre(float* post, float* comb, void* y, const void* residual, mhc
     return MHC_ERR_MISALIGNED;
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.total_bytes) return MHC_ERR_WORKSPACE;
   if (p.res && !aligned(fn, 16) && n_splits < 0) return MHC_ERR_MISALIGNED;
+  {
+    const size_t e = elem_bytes(dt), N = (size_t)n * (n + 2);
+    if (outputs_overlap({{post, (size_t)T * n * 4}, {comb, (size_t)T * n * n * 4}, {y, (size_t)T * D * e},
+                         {workspace, p.total_bytes}},
+                        {{residual, (size_t)T * n * D * e}, {fn, (size_t)n * D * N * 4}, {hc_scale, 3 * 4},
+                         {bias, N * 4}}))
+      return MHC_ERR_INVALID_ARG;
+  }
   return run_pre(p, post, comb, y, residual, fn, hc_scale, bias, sinkhorn_repeat, eps, workspace,
                  static_cast<hipStream_t>(stream));
 }
@@ -226,10 +258,6 @@ MHC_API int mhc_post_pre(void* out, float* post_next, float* comb_next, void* y_
   if (T == 0) return MHC_OK;
   if (!out || !post_next || !comb_next || !y_next || !h || !residual || !post || !comb || !fn || !hc_scale || !bias)
     return MHC_ERR_INVALID_ARG;
-  const size_t e = dt == MHC_BF16 ? 2 : 4;
-  const size_t res_bytes = (size_t)T * n * D * e;
-  if (overlaps(out, res_bytes, residual, res_bytes) || overlaps(out, res_bytes, h, (size_t)T * D * e))
-    return MHC_ERR_INVALID_ARG;
   if (!aligned(out, 16) || !aligned(h, 16) || !aligned(residual, 16) || !aligned(y_next, 16))
     return MHC_ERR_MISALIGNED;
   if (!aligned(post_next, 4) || !aligned(comb_next, 4) || !aligned(post, 4) || !aligned(comb, 4) ||
@@ -238,6 +266,15 @@ MHC_API int mhc_post_pre(void* out, float* post_next, float* comb_next, void* y_
   const size_t need = fp.total_bytes > pp.total_bytes ? fp.total_bytes : pp.total_bytes;
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return MHC_ERR_WORKSPACE;
   if (fp.res && !aligned(fn, 16) && n_splits < 0) return MHC_ERR_MISALIGNED;
+  {
+    const size_t e = elem_bytes(dt), N = (size_t)n * (n + 2);
+    if (outputs_overlap({{out, (size_t)T * n * D * e}, {post_next, (size_t)T * n * 4},
+                         {comb_next, (size_t)T * n * n * 4}, {y_next, (size_t)T * D * e}, {workspace, need}},
+                        {{h, (size_t)T * D * e}, {residual, (size_t)T * n * D * e}, {post, (size_t)T * n * 4},
+                         {comb, (size_t)T * n * n * 4}, {fn, (size_t)n * D * N * 4}, {hc_scale, 3 * 4},
+                         {bias, N * 4}}))
+      return MHC_ERR_INVALID_ARG;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (fp.res && aligned(fn, 16)) {
     const hipError_t er = launch_post_pre_resident(fp, h, residual, post, comb, out, fn, hc_scale, bias, post_next,
@@ -272,6 +309,13 @@ MHC_API int mhc_post(void* out, const void* h, const void* residual, const float
   if (!out || !h || !residual || !post || !comb) return MHC_ERR_INVALID_ARG;
   if (!aligned(out, 16) || !aligned(h, 16) || !aligned(residual, 16)) return MHC_ERR_MISALIGNED;
   if (!aligned(post, 4) || !aligned(comb, 4)) return MHC_ERR_MISALIGNED;
+  {
+    const size_t e = elem_bytes(dt);
+    if (outputs_overlap({{out, (size_t)T * n * D * e}},
+                        {{h, (size_t)T * D * e}, {residual, (size_t)T * n * D * e}, {post, (size_t)T * n * 4},
+                         {comb, (size_t)T * n * n * 4}}))
+      return MHC_ERR_INVALID_ARG;
+  }
   const hipError_t e = launch_post(h, residual, post, comb, out, dt, T, n, D, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MHC_OK : hip_fail(e);
 }
@@ -291,6 +335,13 @@ MHC_API int mhc_post_combine_norm(void* normalized, void* out_residual, const vo
     return MHC_ERR_MISALIGNED;
   if (!aligned(post, 4) || !aligned(comb, 4) || !aligned(combine_w, 4) || !aligned(norm_weight, 4))
     return MHC_ERR_MISALIGNED;
+  {
+    const size_t e = elem_bytes(dt);
+    if (outputs_overlap({{normalized, (size_t)T * D * e}, {out_residual, (size_t)T * n * D * e}},
+                        {{h, (size_t)T * D * e}, {residual, (size_t)T * n * D * e}, {post, (size_t)T * n * 4},
+                         {comb, (size_t)T * n * n * 4}, {combine_w, (size_t)T * n * 4}, {norm_weight, (size_t)D * 4}}))
+      return MHC_ERR_INVALID_ARG;
+  }
   const hipError_t e = launch_post_combine_norm(normalized, out_residual, h, residual, post, comb, combine_w,
                                                 norm_weight, norm_eps, dt, T, n, D, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MHC_OK : hip_fail(e);

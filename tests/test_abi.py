@@ -54,8 +54,8 @@ def test_status_strings(L):
     assert L.mhc_last_error() == b""
 
 
-def pre(L, T=16, n=4, D=64, dt=BF16, post=A, comb=A, y=A, res=A, fn=A, hc=A, bias=A, repeat=20, eps=1e-6,
-        splits=0, ws=A, ws_bytes=1 << 30):
+def pre(L, T=16, n=4, D=64, dt=BF16, post=A, comb=A + 0x10000, y=A + 0x20000, res=A + 0x30000, fn=A + 0x40000,
+        hc=A + 0x50000, bias=A + 0x60000, repeat=20, eps=1e-6, splits=0, ws=A + 0x100000, ws_bytes=1 << 30):
     return L.mhc_pre(post, comb, y, res, dt, fn, hc, bias, T, n, D, repeat, eps, splits, ws, ws_bytes, None)
 
 
@@ -89,6 +89,13 @@ def test_pre_validation(L):
     need = L.mhc_pre_workspace_bytes(16, 4, 64, 0, BF16)
     assert need > 0
     assert pre(L, ws_bytes=need - 1) == WORKSPACE
+    # outputs that overlap another output, an input or the workspace
+    assert pre(L, comb=A + 0x80) == INVALID                  # comb over post (256 B)
+    assert pre(L, y=A + 0x30000 + 0x1000) == INVALID        # y inside the residual
+    assert pre(L, post=A + 0x40000 + 0x5ff0) == INVALID     # post over the end of fn
+    assert pre(L, y=A + 0x60000 - 0x7f0) == INVALID         # y runs into bias
+    assert pre(L, post=A + 0x100000 + 0x200) == INVALID     # post inside the workspace
+    assert pre(L, ws=A + 0x10000 + 0x300, ws_bytes=need) == INVALID   # workspace over the end of comb
 
 
 def test_pre_plan(L):
@@ -141,7 +148,7 @@ def test_pre_plan(L):
 
 
 def test_post_validation(L):
-    def post(T=4, n=4, D=64, dt=BF16, out=A, h=A, res=A, p=A, c=A):
+    def post(T=4, n=4, D=64, dt=BF16, out=A, h=A + 0x10000, res=A + 0x20000, p=A + 0x30000, c=A + 0x40000):
         return L.mhc_post(out, h, res, p, c, dt, T, n, D, None)
     assert post(T=0) == OK
     assert post(T=-3) == INVALID
@@ -151,6 +158,9 @@ def test_post_validation(L):
     assert post(out=None) == INVALID
     assert post(h=A + 4) == MISALIGNED
     assert post(c=A + 1) == MISALIGNED
+    assert post(res=A + 0x7f0) == INVALID      # out (2 KB) runs into the residual
+    assert post(h=A) == INVALID                # out over h
+    assert post(out=A + 0x30000 - 0x10) == INVALID   # out over post
 
 
 def test_post_pre_validation(L):
@@ -170,8 +180,14 @@ def test_post_pre_validation(L):
     assert pp(dt=F32, sp=-1) == UNSUPPORTED      # the single-pass kernel is bf16 only
     assert pp(h=None) == INVALID
     assert pp(fn=None) == INVALID
-    assert pp(out=B + 0x50000) == INVALID        # out over the residual
-    assert pp(out=B + 0x40000 - 64) == INVALID   # out over h
+    need = L.mhc_pre_workspace_bytes(4, 4, 64, 0, BF16)
+    W = B + 0x200000
+    assert pp(out=B + 0x50000, ws=W, wsb=need) == INVALID        # out over the residual
+    assert pp(out=B + 0x40000 - 64, ws=W, wsb=need) == INVALID   # out over h
+    assert pp(y=B + 0x40000, ws=W, wsb=need) == INVALID          # y_next over h
+    assert pp(cn=B + 0x10000 + 16, ws=W, wsb=need) == INVALID    # comb_next over post_next
+    assert pp(pn=W + 0x100, ws=W, wsb=need) == INVALID           # post_next inside the workspace
+    assert pp(y=B + 0x90000, ws=W, wsb=need) == INVALID          # y_next over hc_scale
     assert pp(y=B + 0x30008) == MISALIGNED
     assert pp(c=B + 0x70001) == MISALIGNED
     assert pp() == WORKSPACE                     # no workspace
@@ -186,7 +202,8 @@ def test_post_pre_validation(L):
 
 
 def test_post_combine_norm_validation(L):
-    def pcn(T=4, n=4, D=64, dt=BF16, nz=A, out=A, h=A, res=A, p=A, c=A, w=A, g=A, eps=1e-6):
+    def pcn(T=4, n=4, D=64, dt=BF16, nz=A, out=A + 0x10000, h=A + 0x20000, res=A + 0x30000, p=A + 0x40000,
+            c=A + 0x50000, w=A + 0x60000, g=A + 0x70000, eps=1e-6):
         return L.mhc_post_combine_norm(nz, out, h, res, p, c, w, g, eps, dt, T, n, D, None)
     assert pcn(T=0) == OK
     assert pcn(T=0, out=None) == OK
@@ -196,6 +213,9 @@ def test_post_combine_norm_validation(L):
     assert pcn(nz=None) == INVALID
     assert pcn(w=None) == INVALID
     assert pcn(out=A + 8) == MISALIGNED
+    assert pcn(nz=A + 0x20000) == INVALID      # normalized over h
+    assert pcn(out=A + 0x100) == INVALID       # out_residual over normalized
+    assert pcn(nz=A + 0x70000 + 0x80) == INVALID   # normalized over norm_weight
     assert pcn(D=8 * 4097) == UNSUPPORTED          # more than 1024 threads x 4 vectors
     assert pcn(D=8 * 4096, T=0) == OK
 
