@@ -112,6 +112,24 @@ def _check(t, shape, dtype, device, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _gpu_device(t, name):
+    """The device of ``t``, which must be a GPU tensor (the kernels dereference its address on the GPU)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} is on {t.device}; the kernels need tensors on a GPU")
+    return t.device
+
+
+def _workspace_bytes(ws, device) -> int:
+    """Size in bytes of a caller's workspace tensor, after checking that the kernels can use it."""
+    if ws.device != device:
+        raise ValueError(f"workspace is on {ws.device}, expected {device}")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return ws.numel() * ws.element_size()
+
+
 def _stream(device, stream):
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream(device)
@@ -132,8 +150,9 @@ def mhc_pre_workspace_bytes(T: int, n: int, D: int, n_splits: int = 0, dtype_cod
 def mhc_pre_sync_timeouts(workspace, residual, n_splits: int = 0, stream=None) -> int:
     """Poll timeouts the last mhc_pre on ``workspace`` (for ``residual``'s shape) recorded. Blocks the host."""
     T, n, D = residual.shape
-    st = lib().mhc_pre_sync_timeouts(_ptr(workspace), workspace.numel(), T, n, D, n_splits, _dtype_code(residual),
-                                     _stream(residual.device, stream))
+    dev = _gpu_device(residual, "residual")
+    st = lib().mhc_pre_sync_timeouts(_ptr(workspace), _workspace_bytes(workspace, dev), T, n, D, n_splits,
+                                     _dtype_code(residual), _stream(dev, stream))
     if st < 0:
         raise MhcError("mhc_pre_sync_timeouts", st)
     return st
@@ -149,7 +168,7 @@ def mhc_pre(residual, fn, hc_scale, bias, *, sinkhorn_repeat: int = 20, eps: flo
     torch = _torch()
     L = lib()
     T, n, D = residual.shape
-    dev = residual.device
+    dev = _gpu_device(residual, "residual")
     dt = _dtype_code(residual)
     N = n * (n + 2)
     _check(residual, (T, n, D), residual.dtype, dev, "residual")
@@ -168,7 +187,7 @@ def mhc_pre(residual, fn, hc_scale, bias, *, sinkhorn_repeat: int = 20, eps: flo
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         workspace[:256].zero_()
     st = L.mhc_pre(_ptr(post), _ptr(comb), _ptr(y), _ptr(residual), dt, _ptr(fn), _ptr(hc_scale), _ptr(bias),
-                   T, n, D, sinkhorn_repeat, eps, n_splits, _ptr(workspace), workspace.numel(),
+                   T, n, D, sinkhorn_repeat, eps, n_splits, _ptr(workspace), _workspace_bytes(workspace, dev),
                    _stream(dev, stream))
     if st != 0:
         raise MhcError("mhc_pre", st)
@@ -179,7 +198,7 @@ def mhc_post(h, residual, post, comb, *, out=None, stream=None):
     """out [T, n, D] = post_j * h + sum_i comb[i, j] * residual_i."""
     torch = _torch()
     T, n, D = residual.shape
-    dev = residual.device
+    dev = _gpu_device(residual, "residual")
     dt = _dtype_code(residual)
     _check(h, (T, D), residual.dtype, dev, "h")
     _check(residual, (T, n, D), residual.dtype, dev, "residual")
@@ -199,7 +218,7 @@ def mhc_post_combine_norm(h, residual, post, comb, combine_w, norm_weight, *, no
     """(normalized [T, D], out [T, n, D] or None): fused post mix + combine + RMSNorm."""
     torch = _torch()
     T, n, D = residual.shape
-    dev = residual.device
+    dev = _gpu_device(residual, "residual")
     dt = _dtype_code(residual)
     _check(h, (T, D), residual.dtype, dev, "h")
     _check(residual, (T, n, D), residual.dtype, dev, "residual")
@@ -237,7 +256,7 @@ def mhc_post_pre(h, residual, post, comb, fn, hc_scale, bias, *, sinkhorn_repeat
     torch = _torch()
     L = lib()
     T, n, D = residual.shape
-    dev = residual.device
+    dev = _gpu_device(residual, "residual")
     dt = _dtype_code(residual)
     N = n * (n + 2)
     _check(h, (T, D), residual.dtype, dev, "h")
@@ -261,7 +280,7 @@ def mhc_post_pre(h, residual, post, comb, fn, hc_scale, bias, *, sinkhorn_repeat
         workspace[:256].zero_()
     st = L.mhc_post_pre(_ptr(out), _ptr(post_next), _ptr(comb_next), _ptr(y), _ptr(h), _ptr(residual), _ptr(post),
                         _ptr(comb), dt, _ptr(fn), _ptr(hc_scale), _ptr(bias), T, n, D, sinkhorn_repeat, eps,
-                        n_splits, _ptr(workspace), workspace.numel(), _stream(dev, stream))
+                        n_splits, _ptr(workspace), _workspace_bytes(workspace, dev), _stream(dev, stream))
     if st != 0:
         raise MhcError("mhc_post_pre", st)
     return out, post_next, comb_next, y

@@ -223,5 +223,18 @@ def test_post_combine_norm_validation(L):
 def test_binding_raises_without_gpu_tensors(L):
     import torch
     x = torch.zeros((2, 4, 8), dtype=torch.bfloat16)
-    with pytest.raises(TypeError):
+    # tensors that live in host memory are refused before any call
+    with pytest.raises(ValueError, match="GPU"):
         mhc.mhc_post(x[:, 0].float(), x, torch.zeros(2, 4), torch.zeros(2, 4, 4))
+    h, p, c = x[:, 0].contiguous(), torch.zeros(2, 4), torch.zeros(2, 4, 4)
+    fn, hc, b = torch.zeros(32, 24), torch.ones(3), torch.zeros(24)
+    with pytest.raises(ValueError, match="GPU"):
+        mhc.mhc_post(h, x, p, c)
+    with pytest.raises(ValueError, match="GPU"):
+        mhc.mhc_pre(x, fn, hc, b)
+    with pytest.raises(ValueError, match="GPU"):
+        mhc.mhc_post_pre(h, x, p, c, fn, hc, b)
+    with pytest.raises(ValueError, match="GPU"):
+        mhc.mhc_post_combine_norm(h, x, p, c, torch.zeros(2, 4), torch.ones(8))
+    with pytest.raises(ValueError, match="GPU"):
+        mhc.mhc_pre_sync_timeouts(torch.zeros(256, dtype=torch.uint8), x)

@@ -384,6 +384,30 @@ def test_error_paths_on_gpu():
     with pytest.raises(mhc.MhcError) as e:
         mhc.mhc_pre(g5["residual"], g5["fn"], g5["hc_scale"], g5["bias"])
     assert e.value.status == -2
+    # outputs over an input are refused before any launch
+    y_in_res = g["residual"].view(-1)[:8 * 64].view(8, 64)
+    with pytest.raises(mhc.MhcError) as e:
+        mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], y=y_in_res)
+    assert e.value.status == -1
+    h = torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda")
+    pin, cin = torch.full((8, 4), 0.5, device="cuda"), torch.full((8, 4, 4), 0.25, device="cuda")
+    out = torch.empty((8, 4, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(mhc.MhcError) as e:
+        mhc.mhc_post_pre(h, g["residual"], pin, cin, g["fn"], g["hc_scale"], g["bias"], out=out,
+                         y=out.view(-1)[8 * 64:16 * 64].view(8, 64))
+    assert e.value.status == -1
+    with pytest.raises(mhc.MhcError) as e:
+        mhc.mhc_post(h, g["residual"], pin, cin, out=g["residual"])
+    assert e.value.status == -1
+    # the binding refuses a workspace the kernels could not use
+    with pytest.raises(ValueError, match="workspace"):
+        mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], workspace=torch.zeros(1 << 20, dtype=torch.uint8))
+    # a workspace of another element type counts its bytes
+    need = mhc.mhc_pre_workspace_bytes(8, 4, 64)
+    ws32 = torch.zeros((need + 3) // 4 + 64, dtype=torch.float32, device="cuda")
+    p32, c32, y32 = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], workspace=ws32)
+    p8, c8, y8 = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"])
+    assert torch.equal(p32, p8) and torch.equal(c32, c8) and torch.equal(y32, y8)
     # T = 0 is a no-op
     z = torch.empty((0, 4, 64), dtype=torch.bfloat16, device="cuda")
     p, c, y = mhc.mhc_pre(z, g["fn"], g["hc_scale"], g["bias"])
