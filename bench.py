@@ -15,7 +15,10 @@ stream around every call (events without the system-scope fence), which gives
 each kernel's average duration. A third pass times the layer boundary as one
 call, mhc_post_pre (post of one layer, then the next layer's pre), on the same
 buffers ("boundary"); at decode sizes also with sixteen boundary calls captured
-in one HIP graph ("graph_of_16_us_per_call").
+in one HIP graph ("graph_of_16_us_per_call"). Last, "cold" times single calls
+of each kind after a 1 GiB read that evicts the caches (median of
+--cold-calls calls), as in a model, where the block between pre and post
+evicts the residual that the back-to-back steps leave partly cached.
 
 Prints one JSON line: tokens/s (value), algorithmic HBM GB/s and its fraction
 of the 8 TB/s peak, a roofline object for the dominant kernel (algorithmic
@@ -295,7 +298,13 @@ def run(args):
         cw, nw = dev_t(x.combine_w), dev_t(x.norm_weight)
     tail_bytes = pcn_bytes if fused_tail else post_bytes
     per_set = pre_bytes(T, n, D, e) + tail_bytes(T, n, D, e)
-    nsets = max(2, min(8, int(3 * 256e6 // max(per_set, 1)) + 1))
+    # Between two uses of a buffer set the other sets move at least twice the
+    # 256 MB Infinity Cache (with two sets of this workload's 292 MB, pre read
+    # residual lines the step before last had left there: 45.5 against
+    # 49.3 us). Decode-sized sets stay cached whatever the rotation.
+    nsets = max(3, min(8, -(-int(2 * 256e6) // max(per_set, 1)) + 1))
+    if args.sets:
+        nsets = args.sets
     sets = []
     for k in range(nsets):
         res = dev_t(x.residual) if k == 0 else sets[0]["residual"].clone()
@@ -447,6 +456,38 @@ def run(args):
         boundary["graph_of_16_us_per_call"] = (time.perf_counter() - t4) * 1e6 / (reps * layers)
         del gr
 
+    # Cold calls: each call after a read of 1 GiB (four times the 256 MB
+    # Infinity Cache, far more than the L2s hold), timed by fence-free events
+    # around the call alone; median over the calls. In a model the block
+    # between a layer's pre and post calls evicts the residual, which the
+    # back-to-back steps above leave partly cached for post. The sweep only
+    # reads: a sweep that writes leaves dirty lines whose write-back then
+    # lands in the timed call.
+    cold = None
+    if args.cold_calls > 0:
+        fa = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+        ev = HipEvents(stream.cuda_stream, 2)
+
+        def cold_us(call):
+            out = []
+            for i in range(args.cold_calls):
+                fa.max()
+                ev.record(0)
+                call(i % nsets)
+                ev.record(1)
+                torch.cuda.synchronize()
+                out.append(ev.elapsed_ms(0, 1) * 1e3)
+            return float(np.median(out))
+
+        cp, cq, cb = cold_us(run_pre), cold_us(run_post), cold_us(run_boundary)
+        ev.destroy()
+        del fa
+        cold = {"calls": args.cold_calls, "flush": "1 GiB read (max over an int32 tensor) before each call",
+                "pre_us": cp, "post_us": cq, "boundary_us": cb,
+                "tokens_per_s": T / ((cp + cq) * 1e-6),
+                "gbps": (pre_bytes(T, n, D, e) + tail_bytes(T, n, D, e)) / ((cp + cq) * 1e-6) / 1e9,
+                "boundary_gbps": bb / (cb * 1e-6) / 1e9}
+
     # practical ceiling: a 1 GiB device-to-device copy kernel on the same stream
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -497,6 +538,7 @@ def run(args):
         "hbm_frac_of_copy": step_gbps / copy_gbps,
         "tail": "mhc_post_combine_norm (fused, writes out too)" if fused_tail else "mhc_post",
         "boundary": boundary,
+        "cold": cold,
         # the pre call is the longer of the two
         "roofline": {"kernel": pre_kernel, "bound": "hbm", "achieved": pre_gbps,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": pre_gbps / PEAK_HBM_GBPS,
@@ -520,6 +562,9 @@ def main():
     ap.add_argument("--workload", default="prefill-d7168")
     ap.add_argument("--n-splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sets", type=int, default=0, help="buffer sets the steps rotate over (0: by size)")
+    ap.add_argument("--cold-calls", type=int, default=20,
+                    help="calls of each kind timed after a cache-evicting copy (0: skip; profiling runs skip them)")
     ap.add_argument("--graph", action="store_true",
                     help="capture every call in a HIP graph and replay it (measured slower than direct launches here)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

@@ -745,10 +745,19 @@ int occupancy(int n, int cps, bool post) {
   return occ;
 }
 
+// Compute units of the current device, cached per device (256 when no device
+// answers).
 int device_cus() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev < kMaxDev) {
+    const int c = cache[dev].load(std::memory_order_acquire);
+    if (c != 0) return c;
+  }
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+  if (dev < kMaxDev) cache[dev].store(cus, std::memory_order_release);
   return cus;
 }
 

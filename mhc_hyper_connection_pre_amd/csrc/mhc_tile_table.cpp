@@ -2,7 +2,7 @@
 // dtype, token range). Written by mhc_hyper_connection_pre_amd/tune.py; the
 // library's choice (n_splits = 0) takes an entry that covers the call and is
 // valid for it, and its heuristic otherwise.
-// Measured on AMD Radeon Graphics (gfx950, 256 CUs) (2026-12-03 11:43 UTC).
+// Measured on AMD Radeon Graphics (gfx950, 256 CUs) (2026-12-03 12:07 UTC).
 
 #include "mhc_internal.h"
 
@@ -20,8 +20,8 @@ struct TileEntry {
 
 constexpr TileEntry kTable[] = {
     {0, 4, 4096, 0, 1, 181, -128},
-    {0, 4, 4096, 0, 182, 362, -64},
-    {0, 4, 4096, 0, 363, 2147483647, -32},
+    {0, 4, 4096, 0, 182, 724, -64},
+    {0, 4, 4096, 0, 725, 2147483647, -32},
     {1, 4, 4096, 0, 1, 181, -128},
     {1, 4, 4096, 0, 182, 724, -64},
     {1, 4, 4096, 0, 725, 2147483647, -32},

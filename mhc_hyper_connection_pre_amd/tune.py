@@ -7,8 +7,9 @@ Aiter MHC kernel integration analysis", section 3, TileLang kernel tuning).
 Here the choices are the single-pass kernel's slice count S (n_splits = -S,
 D = 32 * cps * S) and the two-pass path's split count (n_splits = S > 0). For
 every (op, n, D, dtype) and every token count T of a sweep, each candidate is
-timed over back-to-back calls that alternate between two input sets (so the
-Infinity Cache does not serve a repeated input), between two HIP events on the
+timed over back-to-back calls that rotate over input sets (enough of them
+that the other sets move twice the 256 MB Infinity Cache between two uses of
+one, so it does not serve a repeated input), between two HIP events on the
 launch stream, in several rounds that visit the candidates in turn; a
 candidate's time is its median over the rounds. The fastest becomes the table
 entry for the token range around T (range ends at the geometric means of
@@ -60,8 +61,14 @@ def candidates(op: str, T: int, n: int, D: int, dt: int) -> list[int]:
     return out
 
 
+def set_count(T: int, n: int, D: int, elem: int) -> int:
+    """Input sets to rotate over: between two uses of one set the others move twice the 256 MB Infinity Cache."""
+    per_set = T * (2 * n + 2) * D * elem   # residual, out, h, y
+    return max(2, min(8, -(-2 * 256 * 10 ** 6 // max(per_set, 1)) + 1))
+
+
 class _Inputs:
-    """Two device input sets (and outputs) of one shape, random values of the workloads' scale."""
+    """Device input sets (and outputs) of one shape, random values of the workloads' scale."""
 
     def __init__(self, torch, T: int, n: int, D: int, dtype, seed: int):
         g = torch.Generator(device="cuda")
@@ -69,7 +76,7 @@ class _Inputs:
         N = n * (n + 2)
         dev = "cuda"
         self.sets = []
-        for _ in range(2):
+        for _ in range(set_count(T, n, D, 2 if dtype == torch.bfloat16 else 4)):
             s = {
                 "residual": torch.randn((T, n, D), generator=g, device=dev).to(dtype),
                 "h": torch.randn((T, D), generator=g, device=dev).to(dtype),
@@ -98,14 +105,15 @@ def _call(op: str, s: dict, n_splits: int, ws) -> None:
 
 def time_candidate(torch, op: str, inputs: _Inputs, n_splits: int, ws, iters: int, warmup: int) -> float:
     """Microseconds per call: `iters` back-to-back calls between two events, after `warmup` calls."""
+    k = len(inputs.sets)
     for i in range(warmup):
-        _call(op, inputs.sets[i % 2], n_splits, ws)
+        _call(op, inputs.sets[i % k], n_splits, ws)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(iters):
-        _call(op, inputs.sets[i % 2], n_splits, ws)
+        _call(op, inputs.sets[i % k], n_splits, ws)
     e1.record()
     e1.synchronize()
     return e0.elapsed_time(e1) * 1000.0 / iters

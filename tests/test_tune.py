@@ -67,3 +67,14 @@ def test_committed_table_matches_its_record():
                 assert L.mhc_pre_splits(p["T"], e["n"], e["D"], 0, e["dt"]) == abs(want)
             else:
                 assert L.mhc_post_pre_fused(p["T"], e["n"], e["D"], 0, e["dt"]) == (1 if want < 0 else 0)
+
+
+def test_input_set_rotation_outruns_the_infinity_cache():
+    from mhc_hyper_connection_pre_amd.tune import set_count
+    for T, n, D in ((2048, 4, 7168), (1024, 4, 4096), (16384, 4, 7168), (32, 4, 5120)):
+        k = set_count(T, n, D, 2)
+        per_set = T * (2 * n + 2) * D * 2
+        assert 2 <= k <= 8
+        # the other sets move at least twice the 256 MB cache, unless the cap of 8 applies
+        assert (k - 1) * per_set >= 2 * 256 * 10 ** 6 or k == 8
+    assert set_count(2048, 4, 7168, 2) == 3
