@@ -5,9 +5,11 @@ One step = mhc_pre on a [T, n, D] residual followed by mhc_post on the same
 residual with the block output h, using the post/comb that pre produced. The
 default workload is prefill with T = 2048 tokens, n = 4 streams, D = 7168
 (bf16), fn fp32 [28672, 24]. Inputs are seeded synthetic data already
-resident in HBM when the timed region starts. Steps rotate over several input
-and output buffer sets so that no step reads data the previous step left in
-the 256 MB Infinity Cache.
+resident in HBM when the timed region starts. Steps rotate over input and
+output buffer sets such that the other sets move at least twice the 256 MB
+Infinity Cache between two uses of one (three sets at the prefill sizes), so
+no step reads inputs an earlier step left there; decode-sized sets stay
+cached whatever the rotation.
 
 Timing: the K timed steps run with nothing between the launches (value,
 ms_per_step); the same K steps then run again with a HIP event on the launch
