@@ -133,7 +133,11 @@ MHC_API int mhc_pre(float* post, float* comb, void* y,
  * the workspace; a workgroup that waits longer than 100 ms gives up (so the
  * call always finishes) and marks the call, whose outputs are then invalid.
  * Always 0 after a two-pass call. The sizes and knobs must be those of that
- * call. For tests and health checks: it blocks the host.
+ * call. For tests and health checks: it blocks the host. The environment
+ * variable MHC_POLL_TICKS (read at each launch) replaces the 100 ms limit by
+ * that many ticks of the 100 MHz wall clock; 0 makes every wait that its first
+ * read does not satisfy give up (a test hook for this path; the call's
+ * outputs are then invalid, and the next call on the workspace is unaffected).
  */
 MHC_API int mhc_pre_sync_timeouts(const void* workspace, size_t workspace_bytes, int64_t T, int n, int64_t D,
                                   int n_splits, mhc_dtype dt, void* stream);

@@ -47,6 +47,7 @@
 // kernel always terminates.
 
 #include <atomic>
+#include <cstdlib>
 #include <type_traits>
 
 #include "mhc_device.h"
@@ -118,6 +119,7 @@ struct ResArgs {
   const float* post_in;
   const float* comb_in;
   uint16_t* out;
+  long long poll_ticks;   // wall-clock ticks a poll waits before the call is marked timed out
 };
 
 template <int NS, int CPS>
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
       count_in(a.status + kStArrive);
       const long long t0 = wall_clock64();
       while (ld_agent(a.status + kStArrive) < (u64)a.P) {
-        if (wall_clock64() - t0 > kPollTicks) {
+        if (wall_clock64() - t0 > a.poll_ticks) {
           st_agent(a.status + kStTimeout, epoch);
           break;
         }
@@ -547,7 +549,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
             accm += tag_val(vv[u]);
           }
           if (__syncthreads_and(ready)) break;
-          if (wall_clock64() - t0 > kPollTicks) {
+          if (wall_clock64() - t0 > a.poll_ticks) {
             if (tid == 0) st_agent(a.status + kStTimeout, epoch);
             break;
           }
@@ -598,7 +600,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
           pre[i] = tag_val(wv[i]);
         }
         if (__all(ready)) break;
-        if (wall_clock64() - t0 > kPollTicks) {
+        if (wall_clock64() - t0 > a.poll_ticks) {
           if (lane == 0) st_agent(a.status + kStTimeout, epoch);
           break;
         }
@@ -818,6 +820,20 @@ struct Launcher {
   }
 };
 
+// Wall-clock ticks (100 MHz) an exchange wait lasts before it gives up: 100 ms,
+// or MHC_POLL_TICKS when that is set to a number >= 0. The variable is a test
+// hook: at 0 every wait not satisfied at its first read gives up, so the
+// time-out path runs while every kernel still exits normally.
+long long poll_ticks() {
+  const char* e = std::getenv("MHC_POLL_TICKS");
+  if (e && *e) {
+    char* end = nullptr;
+    const long long v = std::strtoll(e, &end, 10);
+    if (*end == '\0' && v >= 0) return v;
+  }
+  return kPollTicks;
+}
+
 ResArgs resident_args(const PrePlan& p, const void* residual, const float* fn, const float* hc_scale,
                       const float* bias, float* post, float* comb, void* y, void* workspace, int repeat, float eps) {
   char* ws = static_cast<char*>(workspace);
@@ -844,6 +860,7 @@ ResArgs resident_args(const PrePlan& p, const void* residual, const float* fn, c
   a.repeat = repeat;
   a.eps = eps;
   a.K = (float)p.K;
+  a.poll_ticks = poll_ticks();
   return a;
 }
 }  // namespace

@@ -361,6 +361,30 @@ def test_outputs_fully_written_and_bounded():
         assert torch.isnan(full[used:]).all()
 
 
+def test_exchange_time_out_is_reported_and_the_next_call_recovers(monkeypatch):
+    # The library's poll limit set to 0 ticks: every exchange wait that its first
+    # read does not satisfy gives up (a fresh workspace's grid barrier among
+    # them), so the call is marked timed out while every kernel exits normally.
+    x = W.generate(W.custom(300, 4, 1024, "bf16", seed=11))
+    g = _gpu_inputs(x)
+    s = x.spec
+    need = mhc.mhc_pre_workspace_bytes(s.T, s.n, s.D, -1)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+    monkeypatch.setenv("MHC_POLL_TICKS", "0")
+    _say("  timed-out call (poll limit 0)")
+    mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], n_splits=-1, workspace=ws)
+    assert mhc.mhc_pre_sync_timeouts(ws, g["residual"], -1) == 1
+    monkeypatch.delenv("MHC_POLL_TICKS")
+    # the next call on the same workspace is a normal one
+    post, comb, y = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], sinkhorn_repeat=s.sinkhorn_repeat,
+                                eps=s.eps, n_splits=-1, workspace=ws)
+    assert mhc.mhc_pre_sync_timeouts(ws, g["residual"], -1) == 0
+    op, oc, oy = _oracle_pre(x)
+    assert_close(host(post), op, "gate", "post after a timed-out call")
+    assert_close(host(comb), oc, "gate", "comb after a timed-out call")
+    assert_close(host(y), oy, "tensor", "y after a timed-out call")
+
+
 def test_error_paths_on_gpu():
     x = W.generate(W.custom(8, 4, 64, "bf16", seed=2))
     g = _gpu_inputs(x)
