@@ -10,7 +10,8 @@ is not built, every call raises.
 Functions mirror the C entry points: ``mhc_pre``, ``mhc_post``,
 ``mhc_post_combine_norm``, ``mhc_post_pre`` (the layer boundary: post, then
 the next layer's pre), ``mhc_pre_workspace_bytes``, ``mhc_pre_splits``,
-``mhc_post_pre_fused``.
+``mhc_post_pre_fused``. With ``prepare=True`` the four compute wrappers check
+and marshal once and return a ``PreparedCall`` that repeats the call.
 """
 
 from __future__ import annotations
@@ -21,7 +22,7 @@ import os
 __all__ = [
     "MhcError", "lib", "library_path", "mhc_pre", "mhc_post", "mhc_post_combine_norm",
     "mhc_pre_workspace_bytes", "mhc_pre_splits", "mhc_pre_sync_timeouts", "mhc_post_pre", "mhc_post_pre_fused",
-    "MHC_BF16", "MHC_F32",
+    "MHC_BF16", "MHC_F32", "PreparedCall",
 ]
 
 MHC_BF16 = 0
@@ -138,6 +139,37 @@ def _stream(device, stream):
     return s.cuda_stream
 
 
+class PreparedCall:
+    """One library call with its tensors checked and its C arguments marshalled once.
+
+    Each call of the object launches the entry point again with the same
+    arguments and returns the same output tensors; the library still checks
+    the arguments and plans the launch on every call. For launch loops
+    (decode steps) where the per-call checks of this binding would cost more
+    host time than the kernels take. The tensors (held here, so their memory
+    stays allocated) must keep their storage: an in-place resize or a swapped
+    storage leaves stale pointers.
+    """
+
+    def __init__(self, name, cfn, args, outputs, keep):
+        self.name, self._fn, self._args, self.outputs, self._keep = name, cfn, args, outputs, keep
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            raise MhcError(self.name, st)
+        return self.outputs
+
+
+def _finish(name, cfn, args, outputs, prepare, keep):
+    if prepare:
+        return PreparedCall(name, cfn, args, outputs, keep)
+    st = cfn(*args)
+    if st != 0:
+        raise MhcError(name, st)
+    return outputs
+
+
 def mhc_pre_splits(T: int, n: int, D: int, n_splits: int = 0, dtype_code: int = MHC_BF16) -> int:
     st = lib().mhc_pre_splits(T, n, D, n_splits, dtype_code)
     if st < 0:
@@ -161,11 +193,12 @@ def mhc_pre_sync_timeouts(workspace, residual, n_splits: int = 0, stream=None) -
 
 
 def mhc_pre(residual, fn, hc_scale, bias, *, sinkhorn_repeat: int = 20, eps: float = 1e-6, n_splits: int = 0,
-            post=None, comb=None, y=None, workspace=None, stream=None):
+            post=None, comb=None, y=None, workspace=None, stream=None, prepare: bool = False):
     """post [T, n] f32, comb [T, n, n] f32, y [T, D] = mhc_pre(residual [T, n, D], fn, hc_scale, bias).
 
     n_splits as in ``include/mhc.h``: 0 = the library's tiling (its tile table, else a heuristic), S > 0 = the
     two-pass path with S split-K partials, -1 = the single-pass kernel, -S = the single-pass kernel with S slices.
+    prepare=True returns a ``PreparedCall`` that makes this call when called.
     """
     torch = _torch()
     L = lib()
@@ -188,16 +221,14 @@ def mhc_pre(residual, fn, hc_scale, bias, *, sinkhorn_repeat: int = 20, eps: flo
         need = L.mhc_pre_workspace_bytes(T, n, D, n_splits, dt)
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         workspace[:256].zero_()
-    st = L.mhc_pre(_ptr(post), _ptr(comb), _ptr(y), _ptr(residual), dt, _ptr(fn), _ptr(hc_scale), _ptr(bias),
-                   T, n, D, sinkhorn_repeat, eps, n_splits, _ptr(workspace), _workspace_bytes(workspace, dev),
-                   _stream(dev, stream))
-    if st != 0:
-        raise MhcError("mhc_pre", st)
-    return post, comb, y
+    args = (_ptr(post), _ptr(comb), _ptr(y), _ptr(residual), dt, _ptr(fn), _ptr(hc_scale), _ptr(bias),
+            T, n, D, sinkhorn_repeat, eps, n_splits, _ptr(workspace), _workspace_bytes(workspace, dev),
+            _stream(dev, stream))
+    return _finish("mhc_pre", L.mhc_pre, args, (post, comb, y), prepare, (residual, fn, hc_scale, bias, workspace))
 
 
-def mhc_post(h, residual, post, comb, *, out=None, stream=None):
-    """out [T, n, D] = post_j * h + sum_i comb[i, j] * residual_i."""
+def mhc_post(h, residual, post, comb, *, out=None, stream=None, prepare: bool = False):
+    """out [T, n, D] = post_j * h + sum_i comb[i, j] * residual_i (prepare=True: a ``PreparedCall``)."""
     torch = _torch()
     T, n, D = residual.shape
     dev = _gpu_device(residual, "residual")
@@ -208,16 +239,14 @@ def mhc_post(h, residual, post, comb, *, out=None, stream=None):
     _check(comb, (T, n, n), torch.float32, dev, "comb")
     out = torch.empty_like(residual) if out is None else out
     _check(out, (T, n, D), residual.dtype, dev, "out")
-    st = lib().mhc_post(_ptr(out), _ptr(h), _ptr(residual), _ptr(post), _ptr(comb), dt, T, n, D,
-                        _stream(dev, stream))
-    if st != 0:
-        raise MhcError("mhc_post", st)
-    return out
+    args = (_ptr(out), _ptr(h), _ptr(residual), _ptr(post), _ptr(comb), dt, T, n, D, _stream(dev, stream))
+    return _finish("mhc_post", lib().mhc_post, args, out, prepare, (h, residual, post, comb))
 
 
 def mhc_post_combine_norm(h, residual, post, comb, combine_w, norm_weight, *, norm_eps: float = 1e-6,
-                          write_out: bool = True, normalized=None, out=None, stream=None):
-    """(normalized [T, D], out [T, n, D] or None): fused post mix + combine + RMSNorm."""
+                          write_out: bool = True, normalized=None, out=None, stream=None, prepare: bool = False):
+    """(normalized [T, D], out [T, n, D] or None): fused post mix + combine + RMSNorm (prepare=True: a
+    ``PreparedCall``)."""
     torch = _torch()
     T, n, D = residual.shape
     dev = _gpu_device(residual, "residual")
@@ -235,12 +264,10 @@ def mhc_post_combine_norm(h, residual, post, comb, combine_w, norm_weight, *, no
         _check(out, (T, n, D), residual.dtype, dev, "out")
     else:
         out = None
-    st = lib().mhc_post_combine_norm(_ptr(normalized), _ptr(out), _ptr(h), _ptr(residual), _ptr(post), _ptr(comb),
-                                     _ptr(combine_w), _ptr(norm_weight), norm_eps, dt, T, n, D,
-                                     _stream(dev, stream))
-    if st != 0:
-        raise MhcError("mhc_post_combine_norm", st)
-    return normalized, out
+    args = (_ptr(normalized), _ptr(out), _ptr(h), _ptr(residual), _ptr(post), _ptr(comb), _ptr(combine_w),
+            _ptr(norm_weight), norm_eps, dt, T, n, D, _stream(dev, stream))
+    return _finish("mhc_post_combine_norm", lib().mhc_post_combine_norm, args, (normalized, out), prepare,
+                   (h, residual, post, comb, combine_w, norm_weight))
 
 
 def mhc_post_pre_fused(T: int, n: int, D: int, n_splits: int = 0, dtype_code: int = MHC_BF16) -> bool:
@@ -252,9 +279,10 @@ def mhc_post_pre_fused(T: int, n: int, D: int, n_splits: int = 0, dtype_code: in
 
 
 def mhc_post_pre(h, residual, post, comb, fn, hc_scale, bias, *, sinkhorn_repeat: int = 20, eps: float = 1e-6,
-                 n_splits: int = 0, out=None, post_next=None, comb_next=None, y=None, workspace=None, stream=None):
+                 n_splits: int = 0, out=None, post_next=None, comb_next=None, y=None, workspace=None, stream=None,
+                 prepare: bool = False):
     """(out [T, n, D], post' [T, n], comb' [T, n, n], y' [T, D]): mhc_post of the finished layer, then the
-    next layer's mhc_pre (fn, hc_scale, bias) on its result."""
+    next layer's mhc_pre (fn, hc_scale, bias) on its result (prepare=True: a ``PreparedCall``)."""
     torch = _torch()
     L = lib()
     T, n, D = residual.shape
@@ -280,9 +308,8 @@ def mhc_post_pre(h, residual, post, comb, fn, hc_scale, bias, *, sinkhorn_repeat
         need = L.mhc_pre_workspace_bytes(T, n, D, n_splits, dt)
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         workspace[:256].zero_()
-    st = L.mhc_post_pre(_ptr(out), _ptr(post_next), _ptr(comb_next), _ptr(y), _ptr(h), _ptr(residual), _ptr(post),
-                        _ptr(comb), dt, _ptr(fn), _ptr(hc_scale), _ptr(bias), T, n, D, sinkhorn_repeat, eps,
-                        n_splits, _ptr(workspace), _workspace_bytes(workspace, dev), _stream(dev, stream))
-    if st != 0:
-        raise MhcError("mhc_post_pre", st)
-    return out, post_next, comb_next, y
+    args = (_ptr(out), _ptr(post_next), _ptr(comb_next), _ptr(y), _ptr(h), _ptr(residual), _ptr(post), _ptr(comb),
+            dt, _ptr(fn), _ptr(hc_scale), _ptr(bias), T, n, D, sinkhorn_repeat, eps, n_splits, _ptr(workspace),
+            _workspace_bytes(workspace, dev), _stream(dev, stream))
+    return _finish("mhc_post_pre", L.mhc_post_pre, args, (out, post_next, comb_next, y), prepare,
+                   (h, residual, post, comb, fn, hc_scale, bias, workspace))

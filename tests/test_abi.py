@@ -233,6 +233,8 @@ def test_binding_raises_without_gpu_tensors(L):
     with pytest.raises(ValueError, match="GPU"):
         mhc.mhc_pre(x, fn, hc, b)
     with pytest.raises(ValueError, match="GPU"):
+        mhc.mhc_pre(x, fn, hc, b, prepare=True)
+    with pytest.raises(ValueError, match="GPU"):
         mhc.mhc_post_pre(h, x, p, c, fn, hc, b)
     with pytest.raises(ValueError, match="GPU"):
         mhc.mhc_post_combine_norm(h, x, p, c, torch.zeros(2, 4), torch.ones(8))

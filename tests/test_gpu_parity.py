@@ -385,6 +385,39 @@ def test_exchange_time_out_is_reported_and_the_next_call_recovers(monkeypatch):
     assert_close(host(y), oy, "tensor", "y after a timed-out call")
 
 
+def test_prepared_calls_repeat_the_direct_calls():
+    # A PreparedCall checks and marshals once; each call launches the same entry point with the same
+    # arguments, so its outputs are the direct call's bits, call after call.
+    x = W.generate(W.custom(96, 4, 1024, "bf16", seed=21))
+    g = _gpu_inputs(x)
+    s = x.spec
+    post0, comb0, y0 = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], sinkhorn_repeat=s.sinkhorn_repeat,
+                                   eps=s.eps)
+    h = g["h"]
+    out0 = mhc.mhc_post(h, g["residual"], post0, comb0)
+    pp = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], sinkhorn_repeat=s.sinkhorn_repeat, eps=s.eps,
+                     prepare=True)
+    pq = mhc.mhc_post(h, g["residual"], pp.outputs[0], pp.outputs[1], prepare=True)
+    cw = torch.sigmoid(torch.randn((96, 4), device="cuda"))
+    nw = torch.rand(1024, device="cuda") + 0.5
+    n0, o0 = mhc.mhc_post_combine_norm(h, g["residual"], post0, comb0, cw, nw)
+    pc = mhc.mhc_post_combine_norm(h, g["residual"], post0, comb0, cw, nw, prepare=True)
+    b0 = mhc.mhc_post_pre(h, g["residual"], post0, comb0, g["fn"], g["hc_scale"], g["bias"],
+                          sinkhorn_repeat=s.sinkhorn_repeat, eps=s.eps)
+    pb = mhc.mhc_post_pre(h, g["residual"], post0, comb0, g["fn"], g["hc_scale"], g["bias"],
+                          sinkhorn_repeat=s.sinkhorn_repeat, eps=s.eps, prepare=True)
+    for _ in range(3):
+        p1, c1, y1 = pp()
+        o1 = pq()
+        n1, oo1 = pc()
+        b1 = pb()
+        torch.cuda.synchronize()
+        assert torch.equal(p1, post0) and torch.equal(c1, comb0) and torch.equal(y1, y0)
+        assert torch.equal(o1, out0)
+        assert torch.equal(n1, n0) and torch.equal(oo1, o0)
+        assert all(torch.equal(u, v) for u, v in zip(b1, b0))
+
+
 def test_error_paths_on_gpu():
     x = W.generate(W.custom(8, 4, 64, "bf16", seed=2))
     g = _gpu_inputs(x)
