@@ -75,6 +75,8 @@ def _check_post(x, g, post_np, comb_np, tokens=None, what=""):
 SMALL = [(T, n, D, dt, sp) for (T, n, D) in ((1, 4, 8), (7, 4, 264), (33, 4, 1032), (67, 3, 520),
                                              (130, 2, 2056), (17, 1, 72), (5, 4, 4104), (3, 8, 520), (66, 8, 1032))
          for dt in ("bf16", "f32") for sp in (0, 1, 3)]
+# n = 8 at a shape of the tile table (bf16 entries), so n_splits = 0 takes a tabled split count
+SMALL += [(40, 8, 4096, "bf16", sp) for sp in (0, 1, 3)]
 
 
 @pytest.mark.parametrize("T,n,D,dt,sp", SMALL, ids=lambda v: str(v))
