@@ -61,8 +61,11 @@ int make_pre_plan(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, PrePl
   q.ksteps = (int)((q.K + kstep - 1) / kstep);
   if (dt == MHC_BF16) {
     q.NCB = pack_blocks(n);
-    if (n == 8) {   // 11 column blocks: one 16-token tile per wave, four waves (LDS for the wave sums)
-      q.MT = 1;
+    if (n == 8) {   // 11 column blocks, four waves. From 128 tokens on, two 16-token tiles per wave
+                    // (each B fragment from L2 serves 32 tokens; one tile per wave measured 21 % slower
+                    // at T = 2048, D = 7168; four tiles' LDS wave sums, 181 KB, would not fit); below
+                    // that one tile per wave, which keeps more workgroups (2.3 us faster at T = 16)
+      q.MT = T >= 128 ? 2 : 1;
       q.NW = 4;
     } else if (n_splits == 1) {  // one split: a tall workgroup of 16 waves per 16 tokens keeps the k-loop parallel
       q.MT = 1;

@@ -257,8 +257,11 @@ hipError_t launch_pre_gemm(const PrePlan& p, const void* residual, const void* f
   }
   const uint16_t* x = static_cast<const uint16_t*>(residual);
   const u32x4* f = static_cast<const u32x4*>(fnp);
-  if (p.n == 8) {   // 11 column blocks: one 16-token tile per wave, four waves
-    launch_gemm_bf16<1, 4, pack_blocks(8)>(p, x, f, part, s);
+  if (p.n == 8) {   // 11 column blocks, four waves, MT 16-token tiles per wave
+    if (p.MT == 2)
+      launch_gemm_bf16<2, 4, pack_blocks(8)>(p, x, f, part, s);
+    else
+      launch_gemm_bf16<1, 4, pack_blocks(8)>(p, x, f, part, s);
     return hipGetLastError();
   }
   if (p.MT == 1) return launch_gemm_bf16_ncb<1, 16>(p, x, f, part, s);
