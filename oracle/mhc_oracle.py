@@ -301,47 +301,22 @@ def rms_norm(c, weight, eps: float) -> np.ndarray:
     return (c * q) * np.asarray(weight, dtype=np.float64)
 
 
-def fma32(a, b, c) -> np.ndarray:
-    """fp32 fused multiply-add round_f32(a * b + c), evaluated through float64.
-
-    The product of two fp32 values is exact in float64; the float64 sum is
-    exact unless the operands are about 2^21 apart in magnitude, where its
-    rounding is far below one fp32 unit, so the result is the correctly
-    rounded fp32 FMA except in (unobserved) double-rounding ties.
-    """
-    return (np.asarray(a, dtype=np.float32).astype(np.float64) * np.asarray(b, dtype=np.float32).astype(np.float64)
-            + np.asarray(c, dtype=np.float32).astype(np.float64)).astype(np.float32)
-
-
 def combine_intermediates(h, x, post, comb, w, dtype: str):
-    """The fused kernel's rounded intermediates (o [T, n, D], c [T, D]) as float64.
+    """The fused tail's stored intermediates (o [T, n, D], c [T, D]) as float64.
 
-    [P2] section 1: the post rows and the combined row are bf16 intermediates.
-    Reading: rounding a value to the storage type is a quantisation decision,
-    so it is taken from the same fp32 sums on both sides: each post row is
-    a = post_j * h, then a = fma(comb[i, j], x_i, a) for i = 0..n-1, rounded
-    to the storage type; the combined row is c = fma(w_j, o_j, c) for
-    j = 0..n-1 from c = 0, rounded to the storage type. (The all-float64 form
-    of the same formulas agrees to within the rounding of these
-    intermediates; a pin checks that bound.)
+    [P2] section 1: the post rows and the combined row are bf16 intermediates
+    (the ``collapsed`` row is a bf16 buffer).
+    Reading: each post row o_j is exactly what ``mhc_post`` stores (the
+    float64 post mix rounded once to the storage type); the combined row is
+    c = sum_j w_j * o_j, formed in float64 from those stored rows and rounded
+    once to the storage type.
     """
-    h32 = decode(h, dtype).astype(np.float32)
-    x32 = decode(x, dtype).astype(np.float32)
-    T, n, D = x32.shape
-    p32 = np.asarray(post, dtype=np.float32)
-    c32 = np.asarray(comb, dtype=np.float32)
-    w32 = np.asarray(w, dtype=np.float32)
-    o = np.empty((T, n, D), dtype=np.float64)
-    for j in range(n):
-        a = (p32[:, j:j + 1].astype(np.float64) * h32.astype(np.float64)).astype(np.float32)
-        for i in range(n):
-            a = fma32(c32[:, i, j:j + 1], x32[:, i, :], a)
-        o[:, j, :] = decode(encode(a, dtype), dtype)
-    acc = np.zeros((T, D), dtype=np.float32)
-    for j in range(n):
-        acc = fma32(w32[:, j:j + 1], o[:, j, :], acc)
-    c = decode(encode(acc, dtype), dtype)
-    return o, c
+    hv = decode(h, dtype)
+    xv = decode(x, dtype)
+    o = decode(encode(post_mix(hv, xv, np.asarray(post, dtype=np.float32).astype(np.float64),
+                               np.asarray(comb, dtype=np.float32).astype(np.float64)), dtype), dtype)
+    c = np.einsum("tj,tjd->td", np.asarray(w, dtype=np.float32).astype(np.float64), o)
+    return o, decode(encode(c, dtype), dtype)
 
 
 def mhc_post_combine_norm(h, residual, post, comb, combine_w, norm_weight, *,
@@ -351,11 +326,11 @@ def mhc_post_combine_norm(h, residual, post, comb, combine_w, norm_weight, *,
     [P2] section 1: one row at a time, the post result is combined across the
     n streams into a bf16 ``collapsed`` row of D values, which is then
     RMS-normalised; [P2] section 2 stores it as ``normalized``.
-    Reading: out_j is the post result rounded to the residual dtype and c is
-    the combined row rounded to the residual dtype, both formed as
-    ``combine_intermediates`` states; the RMSNorm runs in float64 on that
-    rounded c and is rounded once. combine_w [T, n] and norm_weight [D] are
-    fp32.
+    Reading: out_j is the post result rounded to the residual dtype (the
+    same value ``mhc_post`` stores) and c is the combined row rounded to the
+    residual dtype, both formed in float64 as ``combine_intermediates``
+    states; the RMSNorm runs in float64 on that rounded c and is rounded once.
+    combine_w [T, n] and norm_weight [D] are fp32.
     """
     T = np.asarray(residual).shape[0]
     residual = _check_tokens(residual, T, (n, D), "residual")

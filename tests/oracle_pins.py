@@ -319,7 +319,8 @@ def _bf16_val(bits):
 
 
 def pin_combine_norm(O):
-    """One-hot w selects a stream; the norm is torch's rms_norm; brute force with bf16 rounding."""
+    """One-hot w selects a stream; the norm is torch's rms_norm; the fused out is mhc_post's out bit for
+    bit; brute force in float64 scalar loops with bf16 rounding of the post rows and the combined row."""
     g = np.random.default_rng(91)
     T, n, D = 3, 4, 24
     x = _bf16(g.standard_normal((T, n, D)))
@@ -342,35 +343,32 @@ def pin_combine_norm(O):
                                         np.array([[1, 0, 0, 0]], np.float32), gw, n=n, D=D, dtype="bf16",
                                         norm_eps=EPS)
         assert np.array_equal(nz[0], _bf16((cval / math.sqrt(cval * cval + EPS)) * gw.astype(np.float64)))
-    # brute force: scalar loops with the fp32 intermediates and bf16 storage rounding
+    # brute force: float64 scalar loops, each post row and the combined row rounded once to bf16
     w = g.uniform(0, 1, (T, n)).astype(np.float32)
     nz, out = O.mhc_post_combine_norm(h, x, post, comb, w, gw, n=n, D=D, dtype="bf16", norm_eps=EPS)
     for t in range(T):
-        o, c = B.combine_token_f32(_bf16_val(h[t]).tolist(), _bf16_val(x[t]).tolist(), post[t].tolist(),
-                                   comb[t].tolist(), w[t].tolist(), n, D, B.bf16)
+        o = B.post_token(_bf16_val(h[t]).tolist(), _bf16_val(x[t]).tolist(), post[t].astype(np.float64).tolist(),
+                         comb[t].astype(np.float64).tolist(), n, D)
+        o = [[B.bf16(v) for v in row] for row in o]
         assert np.array_equal(_bf16_val(out[t]), np.array(o)), "fused out vs brute"
+        c = [B.bf16(v) for v in B.combine_token(o, w[t].astype(np.float64).tolist(), n, D)]
         ref = B.rms_norm_row(c, gw.astype(np.float64).tolist(), EPS)
-        assert np.array_equal(nz[t], _bf16(np.asarray(ref).astype(np.float32)))
-
-
-def pin_combine_reading_vs_float64(O):
-    """The fp32 intermediates differ from the all-float64 formulas only by storage rounding."""
-    g = np.random.default_rng(92)
-    T, n, D = 16, 4, 512
-    x = _bf16(g.standard_normal((T, n, D)))
-    h = _bf16(g.standard_normal((T, D)))
-    post = g.uniform(0, 1, (T, n)).astype(np.float32)
-    comb = O.sinkhorn(g.standard_normal((T, n, n)), 20).astype(np.float32)
-    w = g.uniform(0, 1, (T, n)).astype(np.float32)
-    gw = g.uniform(0.5, 1.5, D).astype(np.float32)
-    nz, out = O.mhc_post_combine_norm(h, x, post, comb, w, gw, n=n, D=D, dtype="bf16", norm_eps=EPS)
-    o64 = _bf16_val(O.mhc_post(h, x, post, comb, n=n, D=D, dtype="bf16"))
-    ulp_o = np.abs(_bf16_val(out) - o64) / np.maximum(np.abs(o64), 1e-30)
-    assert np.max(ulp_o) <= 2.0 ** -7 and np.mean(ulp_o > 0) < 1e-2, "post rows beyond one bf16 ulp"
-    c64 = _bf16_val(_bf16(np.einsum("tj,tjd->td", w.astype(np.float64), o64).astype(np.float32)))
-    n64 = O.rms_norm(c64, gw, EPS)
-    d = np.abs(_bf16_val(nz) - n64) / np.maximum(np.abs(n64), 1e-3 * np.sqrt(np.mean(n64 ** 2)))
-    assert np.sqrt(np.mean(d ** 2)) < 2e-3 and np.mean(d > 2.0 ** -6) < 1e-3
+        assert np.array_equal(nz[t], _bf16(np.asarray(ref).astype(np.float32))), "normalized vs brute"
+    # the fused call's out is mhc_post's stored result (one definition of the post rows), also at a
+    # size where ties of the rounding are likely to appear
+    T2, D2 = 16, 512
+    x2 = _bf16(g.standard_normal((T2, n, D2)))
+    h2 = _bf16(g.standard_normal((T2, D2)))
+    p2 = g.uniform(0, 1, (T2, n)).astype(np.float32)
+    c2 = O.sinkhorn(g.standard_normal((T2, n, n)), 20).astype(np.float32)
+    w2 = g.uniform(0, 1, (T2, n)).astype(np.float32)
+    g2 = g.uniform(0.5, 1.5, D2).astype(np.float32)
+    nz2, out2 = O.mhc_post_combine_norm(h2, x2, p2, c2, w2, g2, n=n, D=D2, dtype="bf16", norm_eps=EPS)
+    assert np.array_equal(out2, O.mhc_post(h2, x2, p2, c2, n=n, D=D2, dtype="bf16")), "fused out vs mhc_post"
+    cc = _bf16(np.einsum("tj,tjd->td", w2.astype(np.float64), _bf16_val(out2)))
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(_bf16_val(cc)), (D2,),
+                                       torch.from_numpy(g2.astype(np.float64)), EPS)
+    assert np.array_equal(nz2, _bf16(ref.numpy().astype(np.float32))), "normalized vs torch rms_norm"
 
 
 # ---------------------------------------------------------------- layer boundary (post, then the next pre)
@@ -415,5 +413,5 @@ ALL_PINS = [
     pin_brute_pre, pin_brute_post, pin_rounding, pin_rms_closed_form, pin_gemm_onehot_and_groups,
     pin_gates, pin_sinkhorn_exact, pin_sinkhorn_closed_forms, pin_sinkhorn_invariants,
     pin_pre_special_cases, pin_permutation_equivariance, pin_stored_outputs, pin_post_identities,
-    pin_post_orientation, pin_combine_norm, pin_combine_reading_vs_float64, pin_post_pre_boundary,
+    pin_post_orientation, pin_combine_norm, pin_post_pre_boundary,
 ]
