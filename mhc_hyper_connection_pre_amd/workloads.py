@@ -20,8 +20,10 @@ decode-t64-d5120     64       4   5120  bf16  fused post + combine + RMSNorm
 prefill-t16384-d7168 16384    4   7168  bf16  1 % outliers x50; split-K (n_splits > 1)
 ==================== ======== === ===== ===== ==========================================
 
-Distributions: residual and h ~ N(0, 1); fn ~ N(0, fn_std) (the second number
-is the standard deviation); bias ~ N(0, 0.1); hc_scale = (1, 1, 1);
+Distributions: residual ~ N(0, residual_std) (1 in every named workload) and
+h ~ N(0, 1); fn ~ N(0, fn_std) (the second number is the standard deviation);
+bias ~ N(0, 0.1); hc_scale = (1, 1, 1) in every named workload (other values,
+like other repeat counts and eps, are parity cases of the knobs);
 combine_w ~ U(0, 1); norm_weight ~ U(0.5, 1.5). The outlier workload multiplies
 each residual element by 50 with probability 0.01 (a Bernoulli mask) before
 rounding. Values are drawn in float32 and rounded to bf16 to nearest even.
@@ -57,6 +59,8 @@ class Spec:
     bias_std: float = 0.1
     outlier_p: float = 0.0
     outlier_scale: float = 50.0
+    hc_scale: tuple = (1.0, 1.0, 1.0)   # (pre, post, comb) group factors
+    residual_std: float = 1.0
     sinkhorn_repeat: int = 20
     eps: float = 1e-6
     norm_eps: float = 1e-6
@@ -137,12 +141,14 @@ def _store(a32: np.ndarray, dtype: str) -> np.ndarray:
     return f32_to_bf16_bits(a32) if dtype == "bf16" else np.ascontiguousarray(a32, dtype=np.float32)
 
 
-def _token_tensor(rng, T: int, tail: tuple, dtype: str, outlier_rng=None, p=0.0, scale=1.0):
-    """N(0, 1) tensor [T, *tail] drawn in fixed token chunks, optionally with outliers."""
+def _token_tensor(rng, T: int, tail: tuple, dtype: str, outlier_rng=None, p=0.0, scale=1.0, std=1.0):
+    """N(0, std) tensor [T, *tail] drawn in fixed token chunks, optionally with outliers."""
     out = np.empty((T,) + tail, dtype=np.uint16 if dtype == "bf16" else np.float32)
     for t0 in range(0, T, _CHUNK_TOKENS):
         t1 = min(T, t0 + _CHUNK_TOKENS)
         a = rng.standard_normal((t1 - t0,) + tail, dtype=np.float32)
+        if std != 1.0:
+            a = a * np.float32(std)
         if outlier_rng is not None and p > 0.0:
             mask = outlier_rng.random((t1 - t0,) + tail, dtype=np.float32) < np.float32(p)
             a = np.where(mask, a * np.float32(scale), a)
@@ -154,11 +160,12 @@ def generate(s: Spec) -> Inputs:
     """Draw every input array of workload ``s`` (deterministic in ``s``)."""
     rngs = [np.random.default_rng(c) for c in np.random.SeedSequence(s.seed).spawn(_N_STREAMS)]
     residual = _token_tensor(rngs[_S_RESIDUAL], s.T, (s.n, s.D), s.dtype,
-                             rngs[_S_OUTLIER] if s.outlier_p > 0 else None, s.outlier_p, s.outlier_scale)
+                             rngs[_S_OUTLIER] if s.outlier_p > 0 else None, s.outlier_p, s.outlier_scale,
+                             s.residual_std)
     fn = (rngs[_S_FN].standard_normal((s.K, s.N), dtype=np.float32) * np.float32(s.fn_std)).astype(np.float32)
     bias = (rngs[_S_BIAS].standard_normal((s.N,), dtype=np.float32) * np.float32(s.bias_std)).astype(np.float32)
     h = _token_tensor(rngs[_S_H], s.T, (s.D,), s.dtype)
-    hc_scale = np.ones(3, dtype=np.float32)
+    hc_scale = np.asarray(s.hc_scale, dtype=np.float32)
     combine_w = norm_weight = None
     if s.combine:
         combine_w = rngs[_S_COMBINE_W].random((s.T, s.n), dtype=np.float32)
