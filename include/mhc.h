@@ -112,6 +112,16 @@ MHC_API size_t mhc_pre_workspace_bytes(int64_t T, int n, int64_t D, int n_splits
  *   aligned fn; n_splits = 0 takes it when it can. Otherwise the two-pass
  *   path runs (pack fn, split-K GEMM, then an epilogue that reads the
  *   residual again for y).
+ * Co-residency: the single-pass kernel's workgroups wait for one another, so
+ *   the launch is sized to what the device holds at once (workgroups per CU
+ *   from the occupancy query times the CUs). Work that holds CUs while it
+ *   runs (kernels on other streams or in other processes, CU masking) can
+ *   keep some workgroups from starting; the waiting ones then give up after
+ *   100 ms (see mhc_pre_sync_timeouts). Every output that depends on an
+ *   exchange that did not complete is written as NaN (post, comb and y of
+ *   that token; at the layer boundary post_next, comb_next and y_next, while
+ *   out, which does not depend on the exchange, is still right), so a
+ *   timed-out call cannot pass for a good one.
  * Workspace: device memory of at least mhc_pre_workspace_bytes(...) bytes,
  *   256-byte aligned, owned by the caller, not shared by concurrent calls.
  *   Its first 256 bytes are status words that the single-pass path keeps
@@ -131,13 +141,15 @@ MHC_API int mhc_pre(float* post, float* comb, void* y,
  * (synchronises `stream`, then copies 16 bytes to the host). The single-pass
  * path exchanges partial sums between the workgroups of a token tile through
  * the workspace; a workgroup that waits longer than 100 ms gives up (so the
- * call always finishes) and marks the call, whose outputs are then invalid.
+ * call always finishes), marks the call and writes NaN into the outputs that
+ * depend on the missing values.
  * Always 0 after a two-pass call. The sizes and knobs must be those of that
  * call. For tests and health checks: it blocks the host. The environment
  * variable MHC_POLL_TICKS (read at each launch) replaces the 100 ms limit by
  * that many ticks of the 100 MHz wall clock; 0 makes every wait that its first
- * read does not satisfy give up (a test hook for this path; the call's
- * outputs are then invalid, and the next call on the workspace is unaffected).
+ * read does not satisfy give up (a test hook for this path; the outputs of
+ * the tokens concerned are then NaN, and the next call on the workspace is
+ * unaffected).
  */
 MHC_API int mhc_pre_sync_timeouts(const void* workspace, size_t workspace_bytes, int64_t T, int n, int64_t D,
                                   int n_splits, mhc_dtype dt, void* stream);

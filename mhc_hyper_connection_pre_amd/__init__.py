@@ -16,6 +16,7 @@ and marshal once and return a ``PreparedCall`` that repeats the call.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -133,6 +134,12 @@ def _workspace_bytes(ws, device) -> int:
     return ws.numel() * ws.element_size()
 
 
+def _on(stream):
+    """Allocate (and zero) on the launch stream: the caching allocator then orders any later reuse of the
+    memory after the kernels, and the zeroing runs before them on the same stream."""
+    return _torch().cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _stream(device, stream):
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream(device)
@@ -210,17 +217,18 @@ def mhc_pre(residual, fn, hc_scale, bias, *, sinkhorn_repeat: int = 20, eps: flo
     _check(fn, (n * D, N), torch.float32, dev, "fn")
     _check(hc_scale, (3,), torch.float32, dev, "hc_scale")
     _check(bias, (N,), torch.float32, dev, "bias")
-    post = torch.empty((T, n), dtype=torch.float32, device=dev) if post is None else post
-    comb = torch.empty((T, n, n), dtype=torch.float32, device=dev) if comb is None else comb
-    y = torch.empty((T, D), dtype=residual.dtype, device=dev) if y is None else y
+    with _on(stream):
+        post = torch.empty((T, n), dtype=torch.float32, device=dev) if post is None else post
+        comb = torch.empty((T, n, n), dtype=torch.float32, device=dev) if comb is None else comb
+        y = torch.empty((T, D), dtype=residual.dtype, device=dev) if y is None else y
+        if workspace is None:
+            # a fresh workspace: zeroing the status words makes the kernels clear the rest
+            need = L.mhc_pre_workspace_bytes(T, n, D, n_splits, dt)
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+            workspace[:256].zero_()
     _check(post, (T, n), torch.float32, dev, "post")
     _check(comb, (T, n, n), torch.float32, dev, "comb")
     _check(y, (T, D), residual.dtype, dev, "y")
-    if workspace is None:
-        # a fresh workspace: zeroing the status words makes the kernels clear the rest
-        need = L.mhc_pre_workspace_bytes(T, n, D, n_splits, dt)
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-        workspace[:256].zero_()
     args = (_ptr(post), _ptr(comb), _ptr(y), _ptr(residual), dt, _ptr(fn), _ptr(hc_scale), _ptr(bias),
             T, n, D, sinkhorn_repeat, eps, n_splits, _ptr(workspace), _workspace_bytes(workspace, dev),
             _stream(dev, stream))
@@ -237,7 +245,9 @@ def mhc_post(h, residual, post, comb, *, out=None, stream=None, prepare: bool = 
     _check(residual, (T, n, D), residual.dtype, dev, "residual")
     _check(post, (T, n), torch.float32, dev, "post")
     _check(comb, (T, n, n), torch.float32, dev, "comb")
-    out = torch.empty_like(residual) if out is None else out
+    if out is None:
+        with _on(stream):
+            out = torch.empty_like(residual)
     _check(out, (T, n, D), residual.dtype, dev, "out")
     args = (_ptr(out), _ptr(h), _ptr(residual), _ptr(post), _ptr(comb), dt, T, n, D, _stream(dev, stream))
     return _finish("mhc_post", lib().mhc_post, args, out, prepare, (h, residual, post, comb))
@@ -257,13 +267,15 @@ def mhc_post_combine_norm(h, residual, post, comb, combine_w, norm_weight, *, no
     _check(comb, (T, n, n), torch.float32, dev, "comb")
     _check(combine_w, (T, n), torch.float32, dev, "combine_w")
     _check(norm_weight, (D,), torch.float32, dev, "norm_weight")
-    normalized = torch.empty((T, D), dtype=residual.dtype, device=dev) if normalized is None else normalized
+    with _on(stream):
+        normalized = torch.empty((T, D), dtype=residual.dtype, device=dev) if normalized is None else normalized
+        if write_out:
+            out = torch.empty_like(residual) if out is None else out
+        else:
+            out = None
     _check(normalized, (T, D), residual.dtype, dev, "normalized")
-    if write_out:
-        out = torch.empty_like(residual) if out is None else out
+    if out is not None:
         _check(out, (T, n, D), residual.dtype, dev, "out")
-    else:
-        out = None
     args = (_ptr(normalized), _ptr(out), _ptr(h), _ptr(residual), _ptr(post), _ptr(comb), _ptr(combine_w),
             _ptr(norm_weight), norm_eps, dt, T, n, D, _stream(dev, stream))
     return _finish("mhc_post_combine_norm", lib().mhc_post_combine_norm, args, (normalized, out), prepare,
@@ -296,18 +308,19 @@ def mhc_post_pre(h, residual, post, comb, fn, hc_scale, bias, *, sinkhorn_repeat
     _check(fn, (n * D, N), torch.float32, dev, "fn")
     _check(hc_scale, (3,), torch.float32, dev, "hc_scale")
     _check(bias, (N,), torch.float32, dev, "bias")
-    out = torch.empty_like(residual) if out is None else out
-    post_next = torch.empty((T, n), dtype=torch.float32, device=dev) if post_next is None else post_next
-    comb_next = torch.empty((T, n, n), dtype=torch.float32, device=dev) if comb_next is None else comb_next
-    y = torch.empty((T, D), dtype=residual.dtype, device=dev) if y is None else y
+    with _on(stream):
+        out = torch.empty_like(residual) if out is None else out
+        post_next = torch.empty((T, n), dtype=torch.float32, device=dev) if post_next is None else post_next
+        comb_next = torch.empty((T, n, n), dtype=torch.float32, device=dev) if comb_next is None else comb_next
+        y = torch.empty((T, D), dtype=residual.dtype, device=dev) if y is None else y
+        if workspace is None:
+            need = L.mhc_pre_workspace_bytes(T, n, D, n_splits, dt)
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+            workspace[:256].zero_()
     _check(out, (T, n, D), residual.dtype, dev, "out")
     _check(post_next, (T, n), torch.float32, dev, "post_next")
     _check(comb_next, (T, n, n), torch.float32, dev, "comb_next")
     _check(y, (T, D), residual.dtype, dev, "y")
-    if workspace is None:
-        need = L.mhc_pre_workspace_bytes(T, n, D, n_splits, dt)
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-        workspace[:256].zero_()
     args = (_ptr(out), _ptr(post_next), _ptr(comb_next), _ptr(y), _ptr(h), _ptr(residual), _ptr(post), _ptr(comb),
             dt, _ptr(fn), _ptr(hc_scale), _ptr(bias), T, n, D, sinkhorn_repeat, eps, n_splits, _ptr(workspace),
             _workspace_bytes(workspace, dev), _stream(dev, stream))

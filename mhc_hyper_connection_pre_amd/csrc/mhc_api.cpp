@@ -16,10 +16,19 @@ namespace {
 
 thread_local char g_last_error[256] = "";
 
+}  // namespace
+
 int hip_fail(hipError_t e) {
   std::snprintf(g_last_error, sizeof g_last_error, "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
   return MHC_ERR_HIP;
 }
+
+int fail_with(int status, const char* text) {
+  std::snprintf(g_last_error, sizeof g_last_error, "%s", text);
+  return status;
+}
+
+namespace {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -182,6 +191,39 @@ size_t elem_bytes(mhc_dtype dt) { return dt == MHC_BF16 ? 2 : 4; }
 
 }  // namespace
 
+int pre_call(float* post, float* comb, void* y, const void* residual, mhc_dtype dt, const float* fn,
+             const float* hc_scale, const float* bias, int64_t T, int n, int64_t D, int sinkhorn_repeat, float eps,
+             int n_splits, void* workspace, size_t workspace_bytes, hipStream_t s, WorkspaceProvider provider) {
+  PrePlan p;
+  int st = make_pre_plan(T, n, D, n_splits, dt, &p);
+  if (st != MHC_OK) return st;
+  if (sinkhorn_repeat < 1 || !(eps > 0.0f) || !std::isfinite(eps)) return MHC_ERR_INVALID_ARG;
+  if (T == 0) return MHC_OK;
+  if (!post || !comb || !y || !residual || !fn || !hc_scale || !bias) return MHC_ERR_INVALID_ARG;
+  if (!aligned(y, 16) || !aligned(residual, 16)) return MHC_ERR_MISALIGNED;
+  if (!aligned(post, 4) || !aligned(comb, 4) || !aligned(fn, 4) || !aligned(hc_scale, 4) || !aligned(bias, 4))
+    return MHC_ERR_MISALIGNED;
+  if (provider) {   // the workspace comes from the provider, after every other check
+    if (workspace_bytes < p.total_bytes) return MHC_ERR_WORKSPACE;
+  } else if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.total_bytes) {
+    return MHC_ERR_WORKSPACE;
+  }
+  if (p.res && !aligned(fn, 16) && n_splits < 0) return MHC_ERR_MISALIGNED;
+  {
+    const size_t e = elem_bytes(dt), N = (size_t)n * (n + 2);
+    if (outputs_overlap({{post, (size_t)T * n * 4}, {comb, (size_t)T * n * n * 4}, {y, (size_t)T * D * e},
+                         {provider ? nullptr : workspace, p.total_bytes}},
+                        {{residual, (size_t)T * n * D * e}, {fn, (size_t)n * D * N * 4}, {hc_scale, 3 * 4},
+                         {bias, N * 4}}))
+      return MHC_ERR_INVALID_ARG;
+  }
+  if (provider) {
+    st = provider(s, &workspace);
+    if (st != MHC_OK) return st;
+  }
+  return run_pre(p, post, comb, y, residual, fn, hc_scale, bias, sinkhorn_repeat, eps, workspace, s);
+}
+
 }  // namespace mhc
 
 using namespace mhc;
@@ -225,27 +267,8 @@ MHC_API int mhc_post_pre_fused(int64_t T, int n, int64_t D, int n_splits, mhc_dt
 MHC_API int mhc_pre(float* post, float* comb, void* y, const void* residual, mhc_dtype dt, const float* fn,
                     const float* hc_scale, const float* bias, int64_t T, int n, int64_t D, int sinkhorn_repeat,
                     float eps, int n_splits, void* workspace, size_t workspace_bytes, void* stream) {
-  PrePlan p;
-  int st = make_pre_plan(T, n, D, n_splits, dt, &p);
-  if (st != MHC_OK) return st;
-  if (sinkhorn_repeat < 1 || !(eps > 0.0f) || !std::isfinite(eps)) return MHC_ERR_INVALID_ARG;
-  if (T == 0) return MHC_OK;
-  if (!post || !comb || !y || !residual || !fn || !hc_scale || !bias) return MHC_ERR_INVALID_ARG;
-  if (!aligned(y, 16) || !aligned(residual, 16)) return MHC_ERR_MISALIGNED;
-  if (!aligned(post, 4) || !aligned(comb, 4) || !aligned(fn, 4) || !aligned(hc_scale, 4) || !aligned(bias, 4))
-    return MHC_ERR_MISALIGNED;
-  if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.total_bytes) return MHC_ERR_WORKSPACE;
-  if (p.res && !aligned(fn, 16) && n_splits < 0) return MHC_ERR_MISALIGNED;
-  {
-    const size_t e = elem_bytes(dt), N = (size_t)n * (n + 2);
-    if (outputs_overlap({{post, (size_t)T * n * 4}, {comb, (size_t)T * n * n * 4}, {y, (size_t)T * D * e},
-                         {workspace, p.total_bytes}},
-                        {{residual, (size_t)T * n * D * e}, {fn, (size_t)n * D * N * 4}, {hc_scale, 3 * 4},
-                         {bias, N * 4}}))
-      return MHC_ERR_INVALID_ARG;
-  }
-  return run_pre(p, post, comb, y, residual, fn, hc_scale, bias, sinkhorn_repeat, eps, workspace,
-                 static_cast<hipStream_t>(stream));
+  return pre_call(post, comb, y, residual, dt, fn, hc_scale, bias, T, n, D, sinkhorn_repeat, eps, n_splits, workspace,
+                  workspace_bytes, static_cast<hipStream_t>(stream), nullptr);
 }
 
 MHC_API int mhc_post_pre(void* out, float* post_next, float* comb_next, void* y_next, const void* h,

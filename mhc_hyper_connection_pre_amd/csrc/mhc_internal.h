@@ -92,6 +92,22 @@ hipError_t launch_post_combine_norm(void* normalized, void* out, const void* h, 
                                     const float* norm_weight, float eps, mhc_dtype dt, int64_t T, int n,
                                     int64_t D, hipStream_t s);
 
+// Records a HIP error as this thread's last error text and returns MHC_ERR_HIP.
+int hip_fail(hipError_t e);
+// Records `text` as this thread's last error text and returns `status`.
+int fail_with(int status, const char* text);
+
+// Supplies a workspace address for a pre call once its arguments have passed
+// every check (the static-scratch entry point).
+typedef int (*WorkspaceProvider)(hipStream_t s, void** workspace);
+
+// mhc_pre's checks and launches. With a provider, `workspace` is ignored and
+// `workspace_bytes` is the provider's capacity: the provider is called only
+// after every argument check has passed, right before the launches.
+int pre_call(float* post, float* comb, void* y, const void* residual, mhc_dtype dt, const float* fn,
+             const float* hc_scale, const float* bias, int64_t T, int n, int64_t D, int sinkhorn_repeat, float eps,
+             int n_splits, void* workspace, size_t workspace_bytes, hipStream_t s, WorkspaceProvider provider);
+
 // Largest D the fused combine+norm kernel keeps in registers: 1024 threads x 4 vectors.
 constexpr int64_t kPcnMaxVectors = 1024 * 4;
 

@@ -535,28 +535,32 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
         u64 vv[kLoads];
 #pragma unroll
         for (int u = 0; u < kLoads; ++u) vv[u] = (u64)((ok && sub + SUBS * u < S) ? tag ^ 1u : tag) << 32;
+        bool ready = true;
         for (;;) {
 #pragma unroll
           for (int u = 0; u < kLoads; ++u) {
             const int sp = sub + SUBS * u;
             if (!tag_is(vv[u], tag)) vv[u] = ld_agent(reinterpret_cast<const u64*>(pbase + off0 + (uint32_t)sp * rs8));
           }
-          bool ready = true;
+          ready = true;
           accm = 0.0f;
 #pragma unroll
           for (int u = 0; u < kLoads; ++u) {
             ready = ready && tag_is(vv[u], tag);
             accm += tag_val(vv[u]);
           }
-          if (__syncthreads_and(ready)) break;
-          if (wall_clock64() - t0 > a.poll_ticks) {
-            if (tid == 0) st_agent(a.status + kStTimeout, epoch);
-            break;
-          }
+          // The whole workgroup leaves at the same iteration, once every thread
+          // has its words or has run out of time (each wave reads the clock on
+          // its own, so the decision goes through the barrier's reduction).
+          const bool expired = wall_clock64() - t0 > a.poll_ticks;
+          if (!__syncthreads_or(!ready && !expired)) break;
           __builtin_amdgcn_s_sleep(1);
         }
         gs[(mm * SUBS + sub) * 32 + c] = accm;
-        __syncthreads();
+        // a batch with a word still missing is lost: its tokens get NaN gates
+        // and comb (and through pre, NaN y), so the call's outputs show it
+        const bool lost = __syncthreads_or(!ready);
+        if (lost && tid == 0) st_agent(a.status + kStTimeout, epoch);
         if (w * 4 < TB) {   // wave-uniform: all 64 lanes run the epilogue
           const int tt = w * 4 + q;
           const int e = lane & 15;
@@ -569,11 +573,13 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
           float gate, zc;
           bool act;
           logits16<NS>(v0, v1, kc, a.K, a.eps, gate, zc, act);
+          if (lost) gate = __builtin_nanf("");
           const int64_t tk = (int64_t)tile * kTM + sg + (int64_t)S * (m0 + tt);
           const bool mine = tt < TB && m0 + tt < nmine && tk < T;
           // pre first: the other workgroups of the tile wait for it, not for comb
           if (mine && e < NS) put_tagged(a.prebuf + tk * 4 + e, tag, gate);
-          const float combv = sinkhorn16(zc, act, a.repeat);
+          float combv = sinkhorn16(zc, act, a.repeat);
+          if (lost) combv = __builtin_nanf("");
           if (mine) {
             if (e >= NS && e < 2 * NS) a.post[tk * NS + (e - NS)] = gate;
             if (act) a.comb[tk * NS * NS + (e >> 2) * NS + (e & 3)] = combv;
@@ -600,8 +606,12 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
           pre[i] = tag_val(wv[i]);
         }
         if (__all(ready)) break;
-        if (wall_clock64() - t0 > a.poll_ticks) {
+        if (wall_clock64() - t0 > a.poll_ticks) {   // a scalar read: one decision per wave
           if (lane == 0) st_agent(a.status + kStTimeout, epoch);
+          // a gate that never arrived is NaN, so is y of its token
+#pragma unroll
+          for (int i = 0; i < NS; ++i)
+            if (!tag_is(wv[i], tag)) pre[i] = __builtin_nanf("");
           break;
         }
         __builtin_amdgcn_s_sleep(1);

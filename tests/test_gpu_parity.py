@@ -2,8 +2,8 @@
 
 Small shapes span several tiles and a ragged tail and are compared element by
 element; the named workloads run at full size in the launch configuration the
-benchmark times, compared in full where the oracle finishes in seconds and on
-sampled tokens for the 16384-token prefill.
+benchmark times, compared in full (the 16384-token prefill too, for its own split
+count and the library's; other split counts there on sampled tokens).
 """
 
 import numpy as np
@@ -13,7 +13,7 @@ import torch
 import mhc_hyper_connection_pre_amd as mhc
 from mhc_hyper_connection_pre_amd import workloads as W
 import oracle.mhc_oracle as O
-from parity import assert_close, dev_tensor, host
+from parity import assert_close, check_fused_tail, dev_tensor, host
 
 pytestmark = pytest.mark.gpu
 
@@ -88,6 +88,30 @@ def test_small_pre_post(T, n, D, dt, sp):
     post, comb, y = _check_pre(x, g, sp, what=f"T{T} n{n} D{D} {dt} S{sp}")
     op, oc, _ = _oracle_pre(x)
     _check_post(x, g, op, oc, what=f"T{T} n{n} D{D} {dt}")
+
+
+# n = 8, bf16, from 128 tokens on: the two-pass GEMM with two 16-token tiles per wave, ragged last tile
+# (T not a multiple of 32), at explicit split counts and the library's (tabled at D = 4096)
+N8_TALL = [(T, 8, D, sp) for (T, D) in ((130, 1032), (161, 4096)) for sp in (0, 1, 3, 7)]
+
+
+@pytest.mark.parametrize("T,n,D,sp", N8_TALL, ids=lambda v: str(v))
+def test_n8_two_tiles_per_wave(T, n, D, sp):
+    x = W.generate(W.custom(T, n, D, "bf16", seed=T * 3 + D + sp, fn_std=0.02))
+    g = _gpu_inputs(x)
+    _check_pre(x, g, sp, what=f"n8 T{T} D{D} S{sp}")
+
+
+def test_n8_prefill_sampled():
+    """n = 8 at T = 2048, D = 7168 (the throughput shape with eight streams), library tiling; the oracle on
+    sampled tokens (first, last, both sides of every 32-token tile edge near the start, random)."""
+    x = W.generate(W.custom(2048, 8, 7168, "bf16", seed=808, fn_std=0.01))
+    g = _gpu_inputs(x)
+    rng = np.random.default_rng(8)
+    tokens = np.unique(np.concatenate([[0, 1, 31, 32, 33, 63, 64, 2047], rng.choice(2048, 56, replace=False)]))
+    post, comb, _ = _check_pre(x, g, 0, tokens=tokens, what="n8 T2048 D7168")
+    c = host(comb).astype(np.float64)
+    assert np.all(c >= 0) and np.max(np.abs(c.sum(axis=1) - 1)) <= 1e-5
 
 
 # single-pass path: bf16 with D a multiple of 128 (tiles of 128 tokens, slices of 128)
@@ -207,15 +231,13 @@ def test_small_post_combine_norm(T, n, D, dt):
     x = W.generate(W.custom(T, n, D, dt, seed=5 + T + D, combine=True))
     g = _gpu_inputs(x)
     op, oc, _ = _oracle_pre(x)
-    want_nz, want_out = O.mhc_post_combine_norm(x.h, x.residual, op, oc, x.combine_w, x.norm_weight, n=n, D=D,
-                                                dtype=dt, norm_eps=x.spec.norm_eps)
     for write_out in (True, False):
         nz, out = mhc.mhc_post_combine_norm(g["h"], g["residual"], dev_tensor(op), dev_tensor(oc), g["combine_w"],
                                             g["norm_weight"], norm_eps=x.spec.norm_eps, write_out=write_out)
         torch.cuda.synchronize()
-        assert_close(host(nz), want_nz, "tensor", "normalized")
-        if write_out:
-            assert_close(host(out), want_out, "tensor", "out")
+        e, eo = check_fused_tail(host(nz), host(out) if write_out else None, x.h, x.residual, op, oc, x.combine_w,
+                                 x.norm_weight, dt, x.spec.norm_eps, f"T{T} n{n} D{D} {dt}")
+        _say(f"  T{T} n{n} D{D} {dt} fused (out={write_out}): normalized {e:.2e} (plain metric)")
 
 
 # ---------------------------------------------------------------- named workloads at full size
@@ -231,13 +253,12 @@ def test_tiny_f32_workload():
     assert np.max(np.abs(c.sum(axis=2) - 1)) <= 1e-4
     op, oc, _ = _oracle_pre(x)
     _check_post(x, g, op, oc, what="tiny-f32")
-    want_nz, want_out = O.mhc_post_combine_norm(x.h, x.residual, op, oc, x.combine_w, x.norm_weight, n=s.n, D=s.D,
-                                                dtype=s.dtype, norm_eps=s.norm_eps)
     nz, out = mhc.mhc_post_combine_norm(g["h"], g["residual"], dev_tensor(op), dev_tensor(oc), g["combine_w"],
                                         g["norm_weight"], norm_eps=s.norm_eps)
     torch.cuda.synchronize()
-    assert_close(host(nz), want_nz, "tensor", "tiny normalized")
-    assert_close(host(out), want_out, "tensor", "tiny out")
+    e, eo = check_fused_tail(host(nz), host(out), x.h, x.residual, op, oc, x.combine_w, x.norm_weight, s.dtype,
+                             s.norm_eps, "tiny-f32")
+    assert e <= 1e-3 and eo <= 1e-3, (e, eo)
 
 
 @pytest.mark.parametrize("name,n_splits", [("prefill-d4096", None), ("prefill-d7168", None), ("prefill-d7168", 16),
@@ -263,39 +284,71 @@ def test_decode_workload(name):
     _check_pre(x, g, s.n_splits, what=name)
     op, oc, _ = _oracle_pre(x)
     _check_post(x, g, op, oc, what=name)
-    want_nz, want_out = O.mhc_post_combine_norm(x.h, x.residual, op, oc, x.combine_w, x.norm_weight, n=s.n, D=s.D,
-                                                dtype=s.dtype, norm_eps=s.norm_eps)
     for write_out in (True, False):
         nz, out = mhc.mhc_post_combine_norm(g["h"], g["residual"], dev_tensor(op), dev_tensor(oc), g["combine_w"],
                                             g["norm_weight"], norm_eps=s.norm_eps, write_out=write_out)
         torch.cuda.synchronize()
-        e = assert_close(host(nz), want_nz, "tensor", f"{name} normalized")
-        if write_out:
-            assert_close(host(out), want_out, "tensor", f"{name} out")
-        _say(f"  {name} fused (out={write_out}): normalized {e:.2e}")
+        e, eo = check_fused_tail(host(nz), host(out) if write_out else None, x.h, x.residual, op, oc, x.combine_w,
+                                 x.norm_weight, s.dtype, s.norm_eps, name)
+        _say(f"  {name} fused (out={write_out}): normalized {e:.2e} (plain metric), within the rounding allowance")
+
+
+_C5 = {}
+
+
+def _c5():
+    """The 16384-token prefill (1 % outliers x50): inputs, the oracle's pre on every token, and the oracle's
+    post on seeded mixing weights, computed once for the tests that use them."""
+    if not _C5:
+        s = W.spec("prefill-t16384-d7168")
+        x = W.generate(s)
+        _C5["x"] = x
+        _C5["pre"] = _oracle_pre(x)
+        wp, wc = W.mixing_weights(s)
+        _C5["mix"] = (wp, wc)
+        _C5["out"] = O.mhc_post(x.h, x.residual, wp, wc, n=s.n, D=s.D, dtype=s.dtype)
+    return _C5
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("n_splits", [4, 2, 8, 0])
-def test_large_prefill_sampled(n_splits):
-    s = W.spec("prefill-t16384-d7168", n_splits=n_splits)
-    x = W.generate(s)
+@pytest.mark.parametrize("n_splits", [4, 0, 2, 8])
+def test_large_prefill(n_splits):
+    """T = 16384: every token against the oracle for n_splits 4 (the workload's) and 0 (the library's
+    choice), sampled tokens for 2 and 8; post on seeded weights for every token."""
+    c5 = _c5()
+    x = c5["x"]
+    s = x.spec
     g = _gpu_inputs(x)
-    rng = np.random.default_rng(99)
-    tokens = np.unique(np.concatenate([[0, 1, s.T - 1], rng.choice(s.T, 125, replace=False)]))
-    post, comb, y = _check_pre(x, g, n_splits, tokens=tokens, what=f"T16384 S{n_splits}")
-    full_post, full_comb = host(post), host(comb)
-    # post at full size on seeded weights for every token, checked on the sampled tokens
-    wp, wc = W.mixing_weights(s)
-    out = mhc.mhc_post(g["h"], g["residual"], dev_tensor(wp), dev_tensor(wc))
+    full = n_splits in (4, 0)
+    need = mhc.mhc_pre_workspace_bytes(s.T, s.n, s.D, n_splits, 0)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    ws[:256].zero_()
+    post, comb, y = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], sinkhorn_repeat=s.sinkhorn_repeat,
+                                eps=s.eps, n_splits=n_splits, workspace=ws)
+    assert mhc.mhc_pre_sync_timeouts(ws, g["residual"], n_splits) == 0
     torch.cuda.synchronize()
-    want = O.mhc_post(x.h[tokens], x.residual[tokens], wp[tokens], wc[tokens], n=s.n, D=s.D, dtype=s.dtype)
-    assert_close(host(out)[tokens], want, "tensor", "T16384 out")
-    # properties of the pre outputs that hold at every token
-    c = full_comb.astype(np.float64)
+    hp, hc, hy = host(post), host(comb), host(y)
+    op, oc, oy = c5["pre"]
+    if not full:
+        rng = np.random.default_rng(99)
+        tokens = np.unique(np.concatenate([[0, 1, s.T - 1], rng.choice(s.T, 125, replace=False)]))
+        hp, hc, hy, op, oc, oy = hp[tokens], hc[tokens], hy[tokens], op[tokens], oc[tokens], oy[tokens]
+    e1 = assert_close(hp, op, "gate", f"T16384 S{n_splits} post")
+    e2 = assert_close(hc, oc, "gate", f"T16384 S{n_splits} comb")
+    e3 = assert_close(hy, oy, "tensor", f"T16384 S{n_splits} y")
+    _say(f"  T16384 S{n_splits} ({'all' if full else len(hp)} tokens): post {e1:.2e} comb {e2:.2e} y {e3:.2e}")
+    c = host(comb).astype(np.float64)
     assert np.all(c >= 0) and np.max(np.abs(c.sum(axis=1) - 1)) <= 1e-5
-    assert np.all((full_post > 0) & (full_post < 1))
-    del g, out, y
+    assert np.all((host(post) > 0) & (host(post) < 1))
+    del post, comb, y
+    if n_splits == 4:   # post of the same workload, every token
+        wp, wc = c5["mix"]
+        out = mhc.mhc_post(g["h"], g["residual"], dev_tensor(wp), dev_tensor(wc))
+        torch.cuda.synchronize()
+        e = assert_close(host(out), c5["out"], "tensor", "T16384 out")
+        _say(f"  T16384 post (all tokens): out {e:.2e}")
+        del out
+    del g
 
 
 # ---------------------------------------------------------------- invariants, determinism, edges
@@ -374,9 +427,21 @@ def test_exchange_time_out_is_reported_and_the_next_call_recovers(monkeypatch):
     ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
     monkeypatch.setenv("MHC_POLL_TICKS", "0")
     _say("  timed-out call (poll limit 0)")
-    mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], n_splits=-1, workspace=ws)
+    post, comb, y = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], sinkhorn_repeat=s.sinkhorn_repeat,
+                                eps=s.eps, n_splits=-1, workspace=ws)
     assert mhc.mhc_pre_sync_timeouts(ws, g["residual"], -1) == 1
     monkeypatch.delenv("MHC_POLL_TICKS")
+    # the call's outputs show it: a token whose exchange did not complete has NaN outputs, every other
+    # token is right
+    op, oc, oy = _oracle_pre(x)
+    hp, hc, hy = host(post), host(comb), O.decode(host(y), "bf16")
+    lost = np.isnan(hp).any(axis=1) | np.isnan(hc).reshape(s.T, -1).any(axis=1) | np.isnan(hy).any(axis=1)
+    _say(f"  timed-out call: {int(lost.sum())} of {s.T} tokens NaN")
+    assert lost.any(), "a timed-out call left no NaN output"
+    if (~lost).any():
+        assert_close(hp[~lost], op[~lost], "gate", "post of completed tokens")
+        assert_close(hc[~lost], oc[~lost], "gate", "comb of completed tokens")
+        assert_close(host(y)[~lost], oy[~lost], "tensor", "y of completed tokens")
     # the next call on the same workspace is a normal one
     post, comb, y = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], sinkhorn_repeat=s.sinkhorn_repeat,
                                 eps=s.eps, n_splits=-1, workspace=ws)
@@ -385,6 +450,34 @@ def test_exchange_time_out_is_reported_and_the_next_call_recovers(monkeypatch):
     assert_close(host(post), op, "gate", "post after a timed-out call")
     assert_close(host(comb), oc, "gate", "comb after a timed-out call")
     assert_close(host(y), oy, "tensor", "y after a timed-out call")
+
+
+def test_side_stream_without_workspace():
+    """Calls on a side stream with the binding allocating the outputs and the workspace: they are allocated
+    and cleared on that stream, so memory another stream allocates meanwhile is never theirs."""
+    x = W.generate(W.custom(300, 4, 2048, "bf16", seed=31, fn_std=0.02))
+    s = x.spec
+    g = _gpu_inputs(x)
+    op, oc, oy = _oracle_pre(x)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    results = []
+    for k in range(4):
+        res = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], sinkhorn_repeat=s.sinkhorn_repeat,
+                          eps=s.eps, stream=side)
+        out = mhc.mhc_post(g["h"], g["residual"], res[0], res[1], stream=side)
+        results.append((res, out))
+        # the current stream allocates and writes memory while the side stream's calls run
+        junk = torch.full((1 << 22,), float(k), device="cuda")
+        junk.add_(1.0)
+        del junk
+    side.synchronize()
+    for k, ((p, c, y), out) in enumerate(results):
+        assert_close(host(p), op, "gate", f"side stream {k} post")
+        assert_close(host(c), oc, "gate", f"side stream {k} comb")
+        assert_close(host(y), oy, "tensor", f"side stream {k} y")
+        assert_close(host(out), O.mhc_post(x.h, x.residual, host(p), host(c), n=s.n, D=s.D, dtype=s.dtype),
+                     "tensor", f"side stream {k} out")
 
 
 def test_prepared_calls_repeat_the_direct_calls():
