@@ -11,23 +11,26 @@ Infinity Cache between two uses of one (three sets at the prefill sizes), so
 no step reads inputs an earlier step left there; decode-sized sets stay
 cached whatever the rotation.
 
-Timing: the K timed steps run with nothing between the launches (value,
-ms_per_step; each buffer set's calls are prepared once by the binding, so a
-step's host work is the C calls themselves); the same K steps then run again with a HIP event on the launch
-stream around every call (events without the system-scope fence), which gives
-each kernel's average duration. A third pass times the layer boundary as one
-call, mhc_post_pre (post of one layer, then the next layer's pre), on the same
-buffers ("boundary"); at decode sizes also with sixteen boundary calls captured
-in one HIP graph ("graph_of_16_us_per_call"). Last, "cold" times single calls
-of each kind after a 1 GiB read that evicts the caches (median of
---cold-calls calls), as in a model, where the block between pre and post
-evicts the residual that the back-to-back steps leave partly cached.
+Timing (the headline): K steps, each pre and each post call timed alone by
+HIP events on its launch stream (without the system-scope fence) after a
+read of 1 GiB that evicts the L2s and the 256 MB Infinity Cache, so every
+call reads its inputs from HBM, as in a model, where the block between a
+layer's pre and post evicts the residual; ms_per_step is the mean pre call
+plus the mean post call, value = T / ms_per_step. Each buffer set's calls
+are prepared once by the binding, so a call's host work is the C call
+itself. Then, as extra fields: the same steps back to back with nothing
+between the launches ("back_to_back": post then finds part of the residual
+in the memory-side cache), and the layer boundary as one call, mhc_post_pre
+(post of one layer, then the next layer's pre), back to back and after the
+sweep ("boundary"); at decode sizes also sixteen boundary calls captured in
+one HIP graph ("graph_of_16_us_per_call").
 
 Prints one JSON line: tokens/s (value), algorithmic HBM GB/s and its fraction
 of the 8 TB/s peak, a roofline object for the dominant kernel (algorithmic
-bytes per launch / average launch duration from the events; the pre call,
-with the post call beside it as roofline_tail), the boundary call, and the
-CPU oracle timed on the host as a baseline.
+bytes per launch / mean launch duration from the events; the pre call, with
+the post call beside it as roofline_tail), the boundary call, the SHA-256 of
+every input array, the host's CPU model, the source revision, and the CPU
+oracle timed on the host as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        python bench.py --summarize-rocprof DIR   (summarise rocprofv3 output)
@@ -178,14 +181,30 @@ def write_traffic(fetch_dir, write_dir, command):
         print(f"{fname}: {total / 1e6:.1f} MB per launch (algorithmic {algo[which] / 1e6:.1f} MB)")
 
 
-def summarize_rocprof(d):
-    """Print per-kernel averages from a rocprofv3 output directory (kernel trace and/or counters)."""
+def summarize_rocprof(d, warmup=None, steps=None):
+    """Print per-kernel averages from a rocprofv3 output directory (kernel trace and/or counters).
+
+    With warmup W and steps K (the bench run's own): for each kernel also the average over its dispatches
+    W .. W + K - 1 in start order, the headline pass of bench.py, where each pre and post call runs after a
+    cache sweep ("headline_avg_us")."""
     rows = {}
     for path in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
         for r in csv.DictReader(open(path)):
             rows.setdefault(r["Name"], {}).update(
                 {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+                 "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3,
                  "total_us": float(r["TotalDurationNs"]) / 1e3, "pct": float(r["Percentage"])})
+    if warmup is not None and steps is not None:
+        disp = {}
+        for path in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+            for r in csv.DictReader(open(path)):
+                disp.setdefault(r["Kernel_Name"], []).append(
+                    (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+        for k, v in disp.items():
+            v.sort()
+            sel = [dur for _, dur in v[warmup:warmup + steps]]
+            if len(sel) == steps:
+                rows.setdefault(k, {})["headline_avg_us"] = sum(sel) / len(sel) / 1e3
     for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         acc = {}
         for r in csv.DictReader(open(path)):
@@ -196,6 +215,42 @@ def summarize_rocprof(d):
             rows.setdefault(k, {})[c + "_n"] = len(v)
     for k, v in sorted(rows.items(), key=lambda kv: -kv[1].get("total_us", 0)):
         print(json.dumps({"kernel": k, **v}))
+
+
+# ---------------------------------------------------------------- provenance
+
+def host_info():
+    """CPU model and the CPUs this process may use."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cpus_available": len(os.sched_getaffinity(0))}
+
+
+def revision_info():
+    """The git revision when the tree has its history, and a hash of the product sources either way (a GPU
+    box runs a copy of the tree without .git)."""
+    import subprocess
+    rev = None
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=10)
+        rev = r.stdout.strip() or None if r.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError):
+        rev = None
+    h = hashlib.sha256()
+    for d in (CSRC, os.path.join(ROOT, "include")):
+        for name in sorted(os.listdir(d)):
+            if name.endswith((".hip", ".cpp", ".h")):
+                with open(os.path.join(d, name), "rb") as f:
+                    h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.abspath(__file__), "rb") as f:
+        h.update(b"bench.py\0" + f.read())
+    return {"git": rev, "sources_sha256_16": h.hexdigest()[:16]}
 
 
 # ---------------------------------------------------------------- timing events
@@ -383,24 +438,47 @@ def run(args):
         def run_post(k):
             graphs[k][1].replay()
 
-    # The timed steps: nothing but the calls between the two synchronisations
-    # (an event record between kernels costs the next kernel several us here).
+    # The headline: K steps, each call timed alone after a read of 1 GiB
+    # (four times the 256 MB Infinity Cache, far more than the L2s hold), so
+    # every call reads its inputs from HBM, as in a model, where the block
+    # between a layer's pre and post evicts the residual. HIP events without
+    # the system-scope fence bracket each call on its launch stream (a default
+    # event writes back and invalidates the caches, which slows the kernel
+    # after it); the sweep sits outside them. It only reads: a sweep that
+    # writes leaves dirty lines whose write-back then lands in the timed call.
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    ev = HipEvents(stream.cuda_stream, 4 * args.steps)
+    torch.cuda.synchronize()
+    th0 = time.perf_counter()
+    for i in range(args.steps):
+        flush.max()
+        ev.record(4 * i)
+        run_pre(i % nsets)
+        ev.record(4 * i + 1)
+        flush.max()
+        ev.record(4 * i + 2)
+        run_post(i % nsets)
+        ev.record(4 * i + 3)
+    torch.cuda.synchronize()
+    headline_wall_s = time.perf_counter() - th0
+    pre_cold = [ev.elapsed_ms(4 * i, 4 * i + 1) for i in range(args.steps)]
+    post_cold = [ev.elapsed_ms(4 * i + 2, 4 * i + 3) for i in range(args.steps)]
+    ev.destroy()
+    pre_ms, post_ms = float(np.mean(pre_cold)), float(np.mean(post_cold))
+    ms_per_step = pre_ms + post_ms
+
+    # Back to back: the same K steps with nothing between the launches (post
+    # then reads the residual pre left partly in the memory-side cache)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         run_pre(i % nsets)
         run_post(i % nsets)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-
-    # The same steps again with a HIP event on the launch stream around every
-    # call, for the per-kernel durations. The events skip the system-scope
-    # fence (hipEventDisableSystemFence): a default event writes back and
-    # invalidates the caches, which slows the kernel after it.
+    ms_per_step_b2b = (time.perf_counter() - t0) * 1e3 / args.steps
+    # ... and with an event around every call, for the per-kernel durations
     ev = HipEvents(stream.cuda_stream, 3 * args.steps)
     torch.cuda.synchronize()
-    t2 = time.perf_counter()
     for i in range(args.steps):
         ev.record(3 * i)
         run_pre(i % nsets)
@@ -408,9 +486,8 @@ def run(args):
         run_post(i % nsets)
         ev.record(3 * i + 2)
     torch.cuda.synchronize()
-    ms_per_step_events = (time.perf_counter() - t2) * 1e3 / args.steps
-    pre_ms = sum(ev.elapsed_ms(3 * i, 3 * i + 1) for i in range(args.steps)) / args.steps
-    post_ms = sum(ev.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(args.steps)) / args.steps
+    pre_ms_b2b = sum(ev.elapsed_ms(3 * i, 3 * i + 1) for i in range(args.steps)) / args.steps
+    post_ms_b2b = sum(ev.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(args.steps)) / args.steps
     ev.destroy()
 
     # The layer boundary (mhc_post of one layer, then the next layer's mhc_pre)
@@ -468,37 +545,22 @@ def run(args):
         boundary["graph_of_16_us_per_call"] = (time.perf_counter() - t4) * 1e6 / (reps * layers)
         del gr
 
-    # Cold calls: each call after a read of 1 GiB (four times the 256 MB
-    # Infinity Cache, far more than the L2s hold), timed by fence-free events
-    # around the call alone; median over the calls. In a model the block
-    # between a layer's pre and post calls evicts the residual, which the
-    # back-to-back steps above leave partly cached for post. The sweep only
-    # reads: a sweep that writes leaves dirty lines whose write-back then
-    # lands in the timed call.
-    cold = None
-    if args.cold_calls > 0:
-        fa = torch.ones(1 << 28, dtype=torch.int32, device=dev)
-        ev = HipEvents(stream.cuda_stream, 2)
-
-        def cold_us(call):
-            out = []
-            for i in range(args.cold_calls):
-                fa.max()
-                ev.record(0)
-                call(i % nsets)
-                ev.record(1)
-                torch.cuda.synchronize()
-                out.append(ev.elapsed_ms(0, 1) * 1e3)
-            return float(np.median(out))
-
-        cp, cq, cb = cold_us(run_pre), cold_us(run_post), cold_us(run_boundary)
-        ev.destroy()
-        del fa
-        cold = {"calls": args.cold_calls, "flush": "1 GiB read (max over an int32 tensor) before each call",
-                "pre_us": cp, "post_us": cq, "boundary_us": cb,
-                "tokens_per_s": T / ((cp + cq) * 1e-6),
-                "gbps": (pre_bytes(T, n, D, e) + tail_bytes(T, n, D, e)) / ((cp + cq) * 1e-6) / 1e9,
-                "boundary_gbps": bb / (cb * 1e-6) / 1e9}
+    # the boundary call alone after the same sweep
+    ev = HipEvents(stream.cuda_stream, 2 * args.steps)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        flush.max()
+        ev.record(2 * i)
+        run_boundary(i % nsets)
+        ev.record(2 * i + 1)
+    torch.cuda.synchronize()
+    cb = float(np.mean([ev.elapsed_ms(2 * i, 2 * i + 1) * 1e3 for i in range(args.steps)]))
+    ev.destroy()
+    del flush
+    boundary["us_per_call_back_to_back"] = us_b
+    boundary.update({"us_per_call": cb, "tokens_per_s": T / (cb * 1e-6), "gbps": bb / (cb * 1e-6) / 1e9,
+                     "frac_of_peak": bb / (cb * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                     "vs_pre_plus_post_step": ms_per_step * 1e3 / cb})
 
     # practical ceiling: a 1 GiB device-to-device copy kernel on the same stream
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -518,6 +580,7 @@ def run(args):
     step_gbps = (bp + bq) / (ms_per_step * 1e-3) / 1e9
     post_gbps = bq / (post_ms * 1e-3) / 1e9
     pre_gbps = bp / (pre_ms * 1e-3) / 1e9
+    b2b_gbps = (bp + bq) / (ms_per_step_b2b * 1e-3) / 1e9
     pre_kernel = ("pre_resident_kernel (mhc_pre, one launch)" if single
                   else "mhc_pre (fn pack + split-K GEMM + epilogue launches)")
     tail_kernel = "post_combine_norm_kernel" if fused_tail else "post_kernel (mhc_post)"
@@ -537,20 +600,27 @@ def run(args):
         "config": {"workload": spec.name, "T": T, "n": n, "D": D, "n_splits": S,
                    "path": "single-pass" if single else "two-pass",
                    "sinkhorn_repeat": spec.sinkhorn_repeat, "buffer_sets": nsets,
-                   "launch": "hip-graph replay per call" if args.graph else "direct (C-ABI call per launch)"},
+                   "launch": "hip-graph replay per call" if args.graph else "direct (C-ABI call per launch)",
+                   "timing": "each call after a 1 GiB read sweep (outside the events); ms_per_step = mean pre + "
+                             "mean post call"},
         "hbm_gbps": step_gbps,
         "hbm_frac_of_peak": step_gbps / PEAK_HBM_GBPS,
         "algorithmic_bytes_per_step": bp + bq,
-        "ms_per_step_with_events": ms_per_step_events,
         "pre_us": pre_ms * 1e3,
         "post_us": post_ms * 1e3,
+        "pre_us_median": float(np.median(pre_cold)) * 1e3,
+        "post_us_median": float(np.median(post_cold)) * 1e3,
         "pre_gbps": pre_gbps,
         "post_gbps": post_gbps,
+        "headline_wall_s": headline_wall_s,
+        "back_to_back": {"ms_per_step": ms_per_step_b2b, "tokens_per_s": T / (ms_per_step_b2b * 1e-3),
+                         "hbm_gbps": b2b_gbps, "pre_us": pre_ms_b2b * 1e3, "post_us": post_ms_b2b * 1e3,
+                         "note": "no sweep between calls: post reads residual lines pre left in the memory-side "
+                                 "cache"},
         "copy_gbps_1GiB": copy_gbps,
         "hbm_frac_of_copy": step_gbps / copy_gbps,
         "tail": "mhc_post_combine_norm (fused, writes out too)" if fused_tail else "mhc_post",
         "boundary": boundary,
-        "cold": cold,
         # the pre call is the longer of the two
         "roofline": {"kernel": pre_kernel, "bound": "hbm", "achieved": pre_gbps,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": pre_gbps / PEAK_HBM_GBPS,
@@ -560,6 +630,9 @@ def run(args):
                           "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": post_gbps / PEAK_HBM_GBPS,
                           "traffic": stored_traffic("post") if default_wl and not fused_tail else None,
                           "algorithmic_bytes_per_launch": bq},
+        "inputs_sha256": x.checksums(),
+        "host": host_info(),
+        "revision": revision_info(),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
@@ -575,8 +648,6 @@ def main():
     ap.add_argument("--n-splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets the steps rotate over (0: by size)")
-    ap.add_argument("--cold-calls", type=int, default=20,
-                    help="calls of each kind timed after a cache-evicting copy (0: skip; profiling runs skip them)")
     ap.add_argument("--graph", action="store_true",
                     help="capture every call in a HIP graph and replay it (measured slower than direct launches here)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -587,7 +658,7 @@ def main():
                     help="a line of the command that made the counter passes (recorded in the profile)")
     args = ap.parse_args()
     if args.summarize_rocprof:
-        summarize_rocprof(args.summarize_rocprof)
+        summarize_rocprof(args.summarize_rocprof, args.warmup, args.steps)
         return
     if args.write_traffic:
         write_traffic(*args.write_traffic, args.traffic_command)
