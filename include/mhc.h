@@ -155,6 +155,32 @@ MHC_API int mhc_pre_sync_timeouts(const void* workspace, size_t workspace_bytes,
                                   int n_splits, mhc_dtype dt, void* stream);
 
 /*
+ * mhc_pre_static - mhc_pre for callers that cannot allocate device memory
+ * (code under stream capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, arguments and results as mhc_pre with the
+ * same n_splits (the same bits), but the workspace is a device array inside
+ * the library, MHC_PRE_STATIC_SCRATCH_BYTES (32 MiB) per GPU, held from the
+ * library's load until the process ends. The call allocates nothing.
+ *   Limit: sizes whose mhc_pre_workspace_bytes(T, n, D, n_splits, dt) exceeds
+ *   the array return MHC_ERR_WORKSPACE (mhc_last_error() says so) before any
+ *   launch; at n = 4, D = 7168 that covers T up to 2048 (the single-pass
+ *   exchange takes 200 bytes per token per slice), and T = 0 is a no-op.
+ *   Sharing: every call on a GPU uses that GPU's one array, which keeps the
+ *   last call's contents (the exchange state in its status words carries
+ *   over by design). Calls that overlap on one GPU (other streams, other host
+ *   threads) race on it and must not be made. Arguments are checked as
+ *   mhc_pre checks them, before anything is launched; the first accepted call
+ *   on a device also launches a one-block kernel on `stream`, ahead of its
+ *   own, that clears the array's status words.
+ */
+#define MHC_PRE_STATIC_SCRATCH_BYTES (32u << 20)
+MHC_API int mhc_pre_static(float* post, float* comb, void* y,
+                           const void* residual, mhc_dtype dt,
+                           const float* fn, const float* hc_scale, const float* bias,
+                           int64_t T, int n, int64_t D,
+                           int sinkhorn_repeat, float eps, int n_splits, void* stream);
+
+/*
  * mhc_post - [P1] section 2 (the post call, into a tensor shaped like the
  * residual):
  *   out[t][j][d] = post[t][j] * h[t][d] + sum_i comb[t][i][j] * residual[t][i][d]

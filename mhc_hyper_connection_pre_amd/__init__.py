@@ -23,11 +23,12 @@ import os
 __all__ = [
     "MhcError", "lib", "library_path", "mhc_pre", "mhc_post", "mhc_post_combine_norm",
     "mhc_pre_workspace_bytes", "mhc_pre_splits", "mhc_pre_sync_timeouts", "mhc_post_pre", "mhc_post_pre_fused",
-    "MHC_BF16", "MHC_F32", "PreparedCall",
+    "mhc_pre_static", "MHC_PRE_STATIC_SCRATCH_BYTES", "MHC_BF16", "MHC_F32", "PreparedCall",
 ]
 
 MHC_BF16 = 0
 MHC_F32 = 1
+MHC_PRE_STATIC_SCRATCH_BYTES = 32 << 20   # the library's per-GPU scratch for mhc_pre_static
 
 _LIB = None
 
@@ -71,6 +72,8 @@ def lib() -> ctypes.CDLL:
     L.mhc_pre_sync_timeouts.restype = I
     L.mhc_pre.argtypes = [P, P, P, P, I, P, P, P, I64, I, I64, I, F, I, P, SZ, P]
     L.mhc_pre.restype = I
+    L.mhc_pre_static.argtypes = [P, P, P, P, I, P, P, P, I64, I, I64, I, F, I, P]
+    L.mhc_pre_static.restype = I
     L.mhc_post.argtypes = [P, P, P, P, P, I, I64, I, I64, P]
     L.mhc_post.restype = I
     L.mhc_post_combine_norm.argtypes = [P, P, P, P, P, P, P, P, F, I, I64, I, I64, P]
@@ -233,6 +236,35 @@ def mhc_pre(residual, fn, hc_scale, bias, *, sinkhorn_repeat: int = 20, eps: flo
             T, n, D, sinkhorn_repeat, eps, n_splits, _ptr(workspace), _workspace_bytes(workspace, dev),
             _stream(dev, stream))
     return _finish("mhc_pre", L.mhc_pre, args, (post, comb, y), prepare, (residual, fn, hc_scale, bias, workspace))
+
+
+def mhc_pre_static(residual, fn, hc_scale, bias, *, sinkhorn_repeat: int = 20, eps: float = 1e-6,
+                   n_splits: int = 0, post=None, comb=None, y=None, stream=None):
+    """mhc_pre on the library's own per-GPU scratch (no workspace; the C call allocates nothing).
+
+    For callers that cannot allocate device memory during the call: pass ``post``, ``comb`` and ``y`` (this
+    wrapper allocates them with torch only when they are omitted). Sizes whose workspace exceeds
+    ``MHC_PRE_STATIC_SCRATCH_BYTES`` raise; calls that overlap on one GPU race on the shared scratch.
+    """
+    torch = _torch()
+    T, n, D = residual.shape
+    dev = _gpu_device(residual, "residual")
+    dt = _dtype_code(residual)
+    N = n * (n + 2)
+    _check(residual, (T, n, D), residual.dtype, dev, "residual")
+    _check(fn, (n * D, N), torch.float32, dev, "fn")
+    _check(hc_scale, (3,), torch.float32, dev, "hc_scale")
+    _check(bias, (N,), torch.float32, dev, "bias")
+    with _on(stream):
+        post = torch.empty((T, n), dtype=torch.float32, device=dev) if post is None else post
+        comb = torch.empty((T, n, n), dtype=torch.float32, device=dev) if comb is None else comb
+        y = torch.empty((T, D), dtype=residual.dtype, device=dev) if y is None else y
+    _check(post, (T, n), torch.float32, dev, "post")
+    _check(comb, (T, n, n), torch.float32, dev, "comb")
+    _check(y, (T, D), residual.dtype, dev, "y")
+    args = (_ptr(post), _ptr(comb), _ptr(y), _ptr(residual), dt, _ptr(fn), _ptr(hc_scale), _ptr(bias),
+            T, n, D, sinkhorn_repeat, eps, n_splits, _stream(dev, stream))
+    return _finish("mhc_pre_static", lib().mhc_pre_static, args, (post, comb, y), False, None)
 
 
 def mhc_post(h, residual, post, comb, *, out=None, stream=None, prepare: bool = False):

@@ -98,6 +98,28 @@ def test_pre_validation(L):
     assert pre(L, ws=A + 0x10000 + 0x300, ws_bytes=need) == INVALID   # workspace over the end of comb
 
 
+def test_pre_static_validation(L):
+    """The no-allocation variant: its size limit and mhc_pre's own argument checks, before any launch."""
+    L.mhc_pre_static.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int] + [ctypes.c_void_p] * 3 + [
+        ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+    L.mhc_pre_static.restype = ctypes.c_int
+
+    def st(T=16, n=4, D=64, dt=BF16, splits=0, post=A, repeat=20):
+        return L.mhc_pre_static(post, A + 0x10000, A + 0x20000, A + 0x30000, dt, A + 0x40000, A + 0x50000,
+                                A + 0x60000, T, n, D, repeat, 1e-6, splits, None)
+
+    limit = 32 << 20
+    assert L.mhc_pre_workspace_bytes(2048, 4, 7168, 0, BF16) <= limit     # the throughput shape fits
+    assert L.mhc_pre_workspace_bytes(16384, 4, 7168, 0, BF16) > limit     # the 16384-token prefill does not
+    assert st(T=16384, D=7168) == WORKSPACE
+    assert b"32 MiB" in L.mhc_last_error()
+    assert st(T=0) == OK
+    assert st(n=5) == UNSUPPORTED
+    assert st(D=12) == MISALIGNED
+    assert st(repeat=0) == INVALID
+    assert st(T=-1) == INVALID
+
+
 def test_pre_plan(L):
     # split count: explicit values honoured (capped at the number of 32-wide k-steps), auto is positive
     assert L.mhc_pre_splits(2048, 4, 4096, 1, BF16) == 1
