@@ -111,7 +111,10 @@ MHC_API size_t mhc_pre_workspace_bytes(int64_t T, int n, int64_t D, int n_splits
  *   slice tiling fits (mhc_pre_splits(..., -1, ...) > 0) and a 16-byte
  *   aligned fn; n_splits = 0 takes it when it can. Otherwise the two-pass
  *   path runs (pack fn, split-K GEMM, then an epilogue that reads the
- *   residual again for y).
+ *   residual again for y). The single-pass kernel keeps each workgroup's
+ *   waves in step up to three generations of resident tiles and runs one
+ *   pipeline per wave from four on; the environment variable MHC_STAGGER
+ *   (0 or 1, read at each launch) forces either, as a test hook.
  * Co-residency: the single-pass kernel's workgroups wait for one another, so
  *   the launch is sized to what the device holds at once (workgroups per CU
  *   from the occupancy query times the CUs). Work that holds CUs while it
@@ -147,9 +150,10 @@ MHC_API int mhc_pre(float* post, float* comb, void* y,
  * call. For tests and health checks: it blocks the host. The environment
  * variable MHC_POLL_TICKS (read at each launch) replaces the 100 ms limit by
  * that many ticks of the 100 MHz wall clock; 0 makes every wait that its first
- * read does not satisfy give up (a test hook for this path; the outputs of
- * the tokens concerned are then NaN, and the next call on the workspace is
- * unaffected).
+ * read does not satisfy give up, and -1 makes the call publish every
+ * exchanged value with a stale tag, so that every wait gives up (test hooks
+ * for this path; the outputs of the tokens concerned are then NaN, and the
+ * next call on the workspace is unaffected).
  */
 MHC_API int mhc_pre_sync_timeouts(const void* workspace, size_t workspace_bytes, int64_t T, int n, int64_t D,
                                   int n_splits, mhc_dtype dt, void* stream);

@@ -47,10 +47,10 @@ __global__ __launch_bounds__(kPostThreads) void post_kernel(typename S::elem* __
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
       const int64_t c = base + tid + (int64_t)k * kPostThreads;
-      if (c < nch) {
-        hv[k] = ld16(ht + c * V);
+      if (c < nch) {   // streaming loads: nothing of h or the residual is read twice here
+        hv[k] = ld16_stream(ht + c * V);
 #pragma unroll
-        for (int i = 0; i < NS; ++i) xv[k][i] = ld16(xt + i * D + c * V);
+        for (int i = 0; i < NS; ++i) xv[k][i] = ld16_stream(xt + i * D + c * V);
       }
     }
 #pragma unroll

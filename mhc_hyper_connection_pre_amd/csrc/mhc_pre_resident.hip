@@ -33,6 +33,15 @@
 //   4. every wave reads pre for its 16 tokens and writes y for its slice.
 // A work item waits only for the items of its tile in the same generation,
 // and every workgroup is resident, so every generation completes.
+// The kernel has two instances. Up to three generations the workgroup keeps
+// its waves in step (barriers between the steps; step 3 finalises TB tokens
+// at a time over the whole workgroup). From four generations on (STAG) every
+// wave runs steps 1-4 on its own 16 rows with no workgroup barrier after the
+// prologue: it finalises the tokens of its rows that fall to slice s and
+// polls only for the pre values of its own rows, so waves drift apart and one
+// wave's exchange waits overlap other waves' loads. The environment variable
+// MHC_STAGGER (0 or 1, read at each launch) forces either instance: a test
+// hook, both give results within the same rounding bounds.
 //
 // Exchange protocol: every exchanged value is a 64-bit word, tag (low 32 bits
 // of this call's epoch) in the high half and fp32 bits in the low half,
@@ -69,6 +78,7 @@ constexpr int kMaxAVgprsPost = 144;       // residual + block-output registers (
 constexpr int kLdsMax = 160 * 1024;
 constexpr long long kPollTicks = 10000000LL;  // 100 ms of the 100 MHz wall clock
 constexpr int kCpsList[] = {1, 2, 4, 5, 7, 8, 14};
+constexpr int kStaggerGenerations = 4;    // from this many generations on, waves run their own pipelines
 
 typedef unsigned long long u64;
 
@@ -120,6 +130,7 @@ struct ResArgs {
   const float* comb_in;
   uint16_t* out;
   long long poll_ticks;   // wall-clock ticks a poll waits before the call is marked timed out
+  int stagger;            // many generations: every wave runs its own pipeline (the kernel's STAG instance)
 };
 
 template <int NS, int CPS>
@@ -152,11 +163,11 @@ struct ResShape {
 
 // POST: the layer boundary (mhc_post of the finished layer, then this pre on
 // its result); the GEMM's A operand is the post mix formed in registers.
-template <int NS, int CPS, bool POST>
+template <int NS, int CPS, bool POST, bool STAG>
 __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
   typedef ResShape<NS, CPS> F;
   constexpr int N = F::N, NCB = F::NCB, CW = F::CW, KSW = F::KSW;
-  constexpr int kFirstCols = CPS / 2;   // residual columns issued before the packing
+  constexpr int kFirstCols = CPS / 2;   // without STAG: residual columns issued before the packing
   extern __shared__ u32x4 lds[];
   u32x4* Bl = lds;                                              // B fragments, for every generation
   float* scratch = reinterpret_cast<float*>(lds + F::BBLK * 64);
@@ -187,6 +198,12 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
   u64 epoch = ld_agent(a.status + kStEpoch) + 1;
   if ((unsigned)epoch == 0u) ++epoch;   // tag 0 never matches a zeroed word
   const unsigned tag = (unsigned)epoch;
+  // Tag of the words this call publishes: the call's own, or under the test
+  // hook MHC_POLL_TICKS = -1 the previous epoch's, which no wait of this call
+  // accepts (the hook lives here, away from the polling loops: a test there
+  // kept the limit live in scalar registers and made the compiler re-load
+  // kernel arguments inside the main loop).
+  const unsigned ptag = a.poll_ticks < 0 ? tag - 1u : tag;
   const bool fresh = ld_agent(a.status + kStMarker) != a.marker;
 
   // ---- first use of the workspace for this shape: zero the tag region, then
@@ -259,6 +276,30 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // The pre step issues a tile's residual stream by stream (every column of
+  // stream 0, then of stream 1, ...), the order in which its GEMM consumes it:
+  // consecutive loads of a wave then read neighbouring 64-byte pieces of the
+  // same rows, which a load-only probe of this kernel's launch shape read 10 %
+  // faster than column by column (23.6 against 26.2 us for the two
+  // generations of T = 2048, n = 4, D = 7168). The layer boundary needs every
+  // stream of a column at once (the post mix), so it keeps the column order.
+  auto load_tile = [&](int t) {
+    if constexpr (POST || !STAG) {
+      load_pw(t);
+      load_cols(t, std::integral_constant<int, 0>{}, std::integral_constant<int, CPS>{});
+    } else {
+      const uint16_t* xb = a.x + (int64_t)t * kTM * NS * D + d0;
+      const uint32_t xo = (uint32_t)(lane_row(t) * NS * (int)D + q * 8);
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+#pragma unroll
+        for (int c = 0; c < CPS; ++c) {
+          A[i * CPS + c] = ld16(xb + i * D + xo + c * 32);
+          __builtin_amdgcn_sched_barrier(0);   // issue in exactly this order (the waits depend on it)
+        }
+    }
+  };
+
 
   // Output stores. A lane holds 16 bytes (8 values) of one row of a 32-wide
   // column: row r16, bytes 16 q .. 16 q + 15 of the column. Streaming stores
@@ -318,13 +359,17 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
   // order made the compiler keep a base per column, and spill at the layer
   // boundary, where a reload waits for every residual load in flight).
   // Each packing unit loads its 8 fn rows x VW columns straight into
-  // registers and writes the VW columns' hi, lo (and lo2) fragments.
-  {
+  // registers and writes the VW columns' hi, lo (and lo2) fragments. NT
+  // threads (ptid = 0 .. NT - 1) pack; `between` runs once their fn loads
+  // are issued, ahead of the packing arithmetic.
+  auto pack_fn = [&](auto nt_tag, int ptid, auto&& between) {
+    constexpr int NT = decltype(nt_tag)::value;
+    constexpr int FU = (F::PU + NT - 1) / NT;
     typedef typename std::conditional<F::VW == 4, f32x4, float>::type FV;
-    FV fv[F::FU][8];
+    FV fv[FU][8];
 #pragma unroll
-    for (int uu = 0; uu < F::FU; ++uu) {   // fn is 16-byte aligned (checked on the host)
-      const int u0 = tid + uu * kThreads;
+    for (int uu = 0; uu < FU; ++uu) {   // fn is 16-byte aligned (checked on the host)
+      const int u0 = ptid + uu * NT;
       const int u = u0 < F::PU ? u0 : F::PU - 1;   // no branch: the waits stay exact
       const int g = u % F::NG, jq = u / F::NG;
       const int j = jq >> 2, kk = j / NS, i = j - kk * NS;
@@ -333,22 +378,17 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
       for (int e = 0; e < 8; ++e) fv[uu][e] = *reinterpret_cast<const FV*>(src + e * N);
     }
     __builtin_amdgcn_sched_barrier(0);
-    load_pw(tile);
-    // the first half of the first generation's residual columns goes out
-    // right behind the fn slice (HBM stays busy while B is packed), the rest
-    // once B is in LDS (with all of it queued at once, the whole chip's
-    // residual requests delay the fn slice by more than the packing takes)
-    load_cols(tile, std::integral_constant<int, 0>{}, std::integral_constant<int, kFirstCols>{});
+    between();
     // keep every load issued before the packing (the scheduler would sink the
     // residual loads towards their MFMAs and leave few loads in flight)
     __builtin_amdgcn_sched_barrier(0);
-    for (int z = tid; z < F::PZ; z += kThreads) {
+    for (int z = ptid; z < F::PZ; z += NT) {
       const int jq = z / F::NPAD, col = 2 * N + NS + (z - jq * F::NPAD);
       Bl[((jq >> 2) * NCB + col / 16) * 64 + (jq & 3) * 16 + (col & 15)] = u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int uu = 0; uu < F::FU; ++uu) {
-      const int u = tid + uu * kThreads;
+    for (int uu = 0; uu < FU; ++uu) {
+      const int u = ptid + uu * NT;
       if (u < F::PU) {
         const int g = u % F::NG, jq = u / F::NG;
         u32x4* dst = Bl + (jq >> 2) * NCB * 64 + (jq & 3) * 16;
@@ -372,13 +412,44 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
         }
       }
     }
+  };
+
+  if constexpr (STAG) {
+    // Every wave first loads its part of the fn slice and waits for it: at
+    // that moment no residual load is in flight anywhere on the chip, so fn
+    // arrives at once. The residual of the first tile goes out once B is
+    // packed and published by an LDS-only barrier: issuing 28 loads per wave
+    // blocks the wave until the memory pipeline takes them (about as long as
+    // HBM needs for the whole tile), so loads issued ahead of the packing held
+    // the packing back by up to 9 us.
+    pack_fn(std::integral_constant<int, kThreads>{}, tid, [&] { wait_vm(); });
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    load_tile(tile);
+  } else {
+    // The first columns of the first generation's residual go out right
+    // behind the fn slice (HBM stays busy while B is packed), the rest once B
+    // is in LDS: for one or two generations (decode, T = 2048 at n = 4,
+    // D = 7168) this measured 0.8 - 1.3 us faster per call than waiting for fn
+    // first and issuing the whole tile after the barrier.
+    pack_fn(std::integral_constant<int, kThreads>{}, tid, [&] {
+      load_pw(tile);
+      load_cols(tile, std::integral_constant<int, 0>{}, std::integral_constant<int, kFirstCols>{});
+    });
     __syncthreads();
+    load_cols(tile, std::integral_constant<int, kFirstCols>{}, std::integral_constant<int, CPS>{});
   }
 
-  load_cols(tile, std::integral_constant<int, kFirstCols>{}, std::integral_constant<int, CPS>{});
-
-  // ---- one generation: tile `tile`; NEXT = another tile follows, whose
-  // residual is loaded into the registers that y frees
+  // STAG (long runs of generations): each wave runs its own pipeline, with
+  // no workgroup barrier, finalising the tokens of its own rows. The waves of
+  // a workgroup drift apart (the first waves of a workgroup get their data
+  // first), so one wave's exchange waits fall into other waves' loads: at
+  // T = 16384, n = 4, D = 7168 (16 generations) a call takes 315 us against
+  // 361 us with the workgroup in step. With two generations (T = 2048) the
+  // exchange polls queue behind the other waves' loads in the CU's memory
+  // pipeline and the call is no faster, so short runs keep the workgroup in
+  // step (it finalises together, TB tokens at a time).
   auto generation = [&](auto next_tag) {
     constexpr bool NEXT = decltype(next_tag)::value;
     // this tile's residual slice is in flight (rows past T read the tile's
@@ -400,8 +471,27 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float ss = 0.0f;
+    // Without STAG column by column, in the load order (the layer boundary
+    // forms each column's post mix first). With STAG stream by stream (the
+    // pre step's load order there, load_tile); the layer boundary then first
+    // forms the post mix of every column as its loads land and runs the same
+    // k-step order. Either way the pre step and the layer boundary of one
+    // mode add the products in the same order and give the same bits.
+    // (a macro, not a lambda: a lambda capturing acc by reference cost the
+    // layer-boundary kernel six more spilled registers)
+#define MHC_KSTEP(i, c)                                                                                   \
+  do {                                                                                                    \
+    const u32x4 aw = A[(i) * CPS + (c)];                                                                  \
+    const bf16x8 av = __builtin_bit_cast(bf16x8, aw);                                                     \
+    _Pragma("unroll") for (int cb = 0; cb < NCB; ++cb) acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16( \
+        av, __builtin_bit_cast(bf16x8, Bl[(((c) * NS + (i)) * NCB + cb) * 64 + lane]), acc[cb], 0, 0, 0); \
+    ss = dot2_self(aw.x, ss);                                                                             \
+    ss = dot2_self(aw.y, ss);                                                                             \
+    ss = dot2_self(aw.z, ss);                                                                             \
+    ss = dot2_self(aw.w, ss);                                                                             \
+  } while (0)
 #pragma unroll
-    for (int c = 0; c < CPS; ++c) {   // the load order
+    for (int c = 0; c < ((POST || !STAG) ? CPS : 0); ++c) {
       if constexpr (POST) {
         // column c of the new residual, out_j = post_j h + sum_i comb[i][j]
         // x_i, in fp32 with the operation order and the single rounding of
@@ -430,21 +520,18 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
 #pragma unroll
         for (int jj = 0; jj < NS; ++jj) A[jj * CPS + c] = ov[jj];
       }
+      if constexpr (!STAG) {
 #pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        const int j = i * CPS + c;
-        const u32x4 aw = A[j];
-        const bf16x8 av = __builtin_bit_cast(bf16x8, aw);
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              av, __builtin_bit_cast(bf16x8, Bl[((c * NS + i) * NCB + cb) * 64 + lane]), acc[cb], 0, 0, 0);
-        ss = dot2_self(aw.x, ss);
-        ss = dot2_self(aw.y, ss);
-        ss = dot2_self(aw.z, ss);
-        ss = dot2_self(aw.w, ss);
+        for (int i = 0; i < NS; ++i) MHC_KSTEP(i, c);
       }
     }
+    if constexpr (STAG) {
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+#pragma unroll
+        for (int c = 0; c < CPS; ++c) MHC_KSTEP(i, c);
+    }
+#undef MHC_KSTEP
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
 
@@ -474,10 +561,10 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
         const float hi = rr[c < N ? c : NCB * 16];
         const float lo = rr[c < N ? c + N : 0];
         const float lo2 = rr[c < NS ? c + 2 * N : 0];
-        put_tagged(pw0 + idx, tag, c < NS ? hi + lo + lo2 : (c < N ? hi + lo : hi));
+        put_tagged(pw0 + idx, ptag, c < NS ? hi + lo + lo2 : (c < N ? hi + lo : hi));
       }
     }
-    __syncthreads();   // every wave has published before any finalises
+    if constexpr (!STAG) __syncthreads();   // every wave has published before any finalises
     // layer boundary: out goes to HBM now, while the tile's exchange below
     // leaves HBM mostly idle (stored during the GEMM it competed with the
     // residual loads: 8 us more per call at T = 2048, n = 4, D = 7168)
@@ -505,12 +592,77 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
         for (int jj = 0; jj < NS; ++jj)
           if (rok) st16_stream(ob + jj * D + oo + c * 32, A[jj * CPS + c]);
     }
-    // ---- 3. finalise tokens sg, sg + S, ... of the tile, TB at a time. Thread
-    // (c = tid % 32, group = tid / 32) sums column c of splits sub, sub + SUBS,
-    // ... (sub = group % SUBS) of token group / SUBS of the batch; the SUBS sums
-    // are added in order through LDS; 16-lane group g of wave w then runs the
-    // epilogue of token 4 w + g of the batch.
-    {
+    // ---- 3. finalise the tile's tokens sg, sg + S, ... . With stagger, each
+    // wave finalises those in its own 16 rows: lane (column c = lane % 32,
+    // half = lane / 32) sums column c over slices half, half + 2, ... in order,
+    // the two halves are added, and lanes 0..15 run the epilogue of the token.
+    if constexpr (STAG) {
+      constexpr int kFW = CPS >= 4 ? 16 : 40;   // partial words per lane and round
+      const int S = a.S;
+      int r = (sg - 16 * w) % S;
+      if (r < 0) r += S;
+      const int col = lane & 31, half = lane >> 5;
+      const bool cact = col <= N;
+      const char* pbase = reinterpret_cast<const char*>(a.part);
+      const uint32_t rs8 = (uint32_t)(T * (N + 1) * 8);   // bytes from one slice's words to the next
+      const EpiConst kc = epi_const<NS>(a.hc_scale, a.bias);
+      const long long t0 = wall_clock64();
+      for (; r < 16; r += S) {
+        const int64_t tok = (int64_t)tile * kTM + 16 * w + r;
+        if (tok >= T) break;
+        const uint32_t off0 = (uint32_t)((tok * (N + 1) + (cact ? col : 0)) * 8);
+        float v = 0.0f;
+        bool lost = false;
+        for (int b = 0; b < S; b += 2 * kFW) {
+          // words past the splits (or of an unused column) count as ready; a
+          // poll re-reads only the words not yet ready
+          u64 vv[kFW];
+#pragma unroll
+          for (int u = 0; u < kFW; ++u)
+            vv[u] = (u64)((cact && b + half + 2 * u < S) ? tag ^ 1u : tag) << 32;
+          for (;;) {
+            bool ready = true;
+#pragma unroll
+            for (int u = 0; u < kFW; ++u) {
+              const int sp = b + half + 2 * u;
+              if (!tag_is(vv[u], tag)) vv[u] = ld_agent(reinterpret_cast<const u64*>(pbase + off0 + (uint32_t)sp * rs8));
+            }
+#pragma unroll
+            for (int u = 0; u < kFW; ++u) ready = ready && tag_is(vv[u], tag);
+            
+            if (__all(ready)) break;
+            if (wall_clock64() - t0 > a.poll_ticks) {   // a scalar read: one decision per wave
+              lost = true;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+#pragma unroll
+          for (int u = 0; u < kFW; ++u) v += tag_val(vv[u]);
+        }
+        v += __shfl_xor(v, 32);
+        const float v1 = __shfl(v, (lane & 15) + 16);
+        float gate, zc;
+        bool act;
+        logits16<NS>(v, v1, kc, a.K, a.eps, gate, zc, act);
+        // a token whose words did not all arrive gets NaN gates and comb (and
+        // through pre, NaN y), so the call's outputs show it
+        if (lost) gate = __builtin_nanf("");
+        if (lost && lane == 0) st_agent(a.status + kStTimeout, epoch);
+        if (lane < NS) put_tagged(a.prebuf + tok * 4 + lane, ptag, gate);   // pre first
+        float combv = sinkhorn16(zc, act, a.repeat);
+        if (lost) combv = __builtin_nanf("");
+        if (lane < 16) {
+          if (lane >= NS && lane < 2 * NS) a.post[tok * NS + (lane - NS)] = gate;
+          if (act) a.comb[tok * NS * NS + (lane >> 2) * NS + (lane & 3)] = combv;
+        }
+      }
+    } else {
+      // Without stagger the workgroup finalises them together, TB at a time.
+      // Thread (c = tid % 32, group = tid / 32) sums column c of splits sub,
+      // sub + SUBS, ... (sub = group % SUBS) of token group / SUBS of the
+      // batch; the SUBS sums are added in order through LDS; 16-lane group g
+      // of wave w then runs the epilogue of token 4 w + g of the batch.
       const int TB = a.TB, SUBS = 16 / a.TB;
       // tokens of the tile this workgroup finalises: sg, sg + S, ... below T
       const int64_t left = T - (int64_t)tile * kTM;
@@ -549,6 +701,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
             ready = ready && tag_is(vv[u], tag);
             accm += tag_val(vv[u]);
           }
+          
           // The whole workgroup leaves at the same iteration, once every thread
           // has its words or has run out of time (each wave reads the clock on
           // its own, so the decision goes through the barrier's reduction).
@@ -577,7 +730,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
           const int64_t tk = (int64_t)tile * kTM + sg + (int64_t)S * (m0 + tt);
           const bool mine = tt < TB && m0 + tt < nmine && tk < T;
           // pre first: the other workgroups of the tile wait for it, not for comb
-          if (mine && e < NS) put_tagged(a.prebuf + tk * 4 + e, tag, gate);
+          if (mine && e < NS) put_tagged(a.prebuf + tk * 4 + e, ptag, gate);
           float combv = sinkhorn16(zc, act, a.repeat);
           if (lost) combv = __builtin_nanf("");
           if (mine) {
@@ -605,6 +758,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
           ready = ready && tag_is(wv[i], tag);
           pre[i] = tag_val(wv[i]);
         }
+        
         if (__all(ready)) break;
         if (wall_clock64() - t0 > a.poll_ticks) {   // a scalar read: one decision per wave
           if (lane == 0) st_agent(a.status + kStTimeout, epoch);
@@ -617,20 +771,21 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
         __builtin_amdgcn_s_sleep(1);
       }
     }
-    // y column by column; the registers of a column are refilled with the next
-    // tile's residual right after, so those loads overlap the rest of y
+    // y column by column, each column's registers refilled with the next
+    // tile's residual right after, so those loads overlap the rest of y; the
+    // pre step with STAG forms and stores every column of y first, then
+    // issues the next tile's loads stream by stream.
     {
       uint16_t* yb = a.y + (int64_t)tile * kTM * D + d0;
       const int nlr = lane_row(tile + G);
-      if constexpr (NEXT) load_pw(tile + G);
+      if constexpr (NEXT && POST) load_pw(tile + G);
       const int64_t wrow0 = (int64_t)tile * kTM + w * 16;
       const int wrows = T - wrow0 < 16 ? (int)(T - wrow0) : 16;
       uint16_t* ybw = yb + (uint32_t)(w * 16 * (int)D);
       const int phase = (int)(d0 >> 5) & 1;
       const uint32_t off[2] = {(uint32_t)((lane >> 3) * (int)D + (lane & 7) * 8),
                                (uint32_t)((8 + (lane >> 3)) * (int)D + (lane & 7) * 8)};
-#pragma unroll
-      for (int c = 0; c < CPS; ++c) {
+      auto ycol = [&](int c) {
         float o[8], f[8];
         Vec<BF16>::unpack(A[c], f);
 #pragma unroll
@@ -641,16 +796,37 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
 #pragma unroll
           for (int v = 0; v < 8; ++v) o[v] = fmaf(pre[i], f[v], o[v]);
         }
+        return Vec<BF16>::pack(o);
+      };
+      auto ystore = [&](int c, const u32x4& yv) {
         if constexpr (kUnitStores) {
-          stage_col(0, phase, c, Vec<BF16>::pack(o));
-          if constexpr (NEXT) load_col(tile + G, nlr, c);
+          stage_col(0, phase, c, yv);
 #pragma unroll
           for (int u = 0; u < kUnits; ++u)
             if (c == unit_done(u)) flush_unit(0, phase, u, ybw, off, wrows);
         } else {
-          if (rok) st16_stream(yb + (uint32_t)((w * 16 + r16) * (int)D + q * 8) + c * 32, Vec<BF16>::pack(o));
-          if constexpr (NEXT) load_col(tile + G, nlr, c);
+          if (rok) st16_stream(yb + (uint32_t)((w * 16 + r16) * (int)D + q * 8) + c * 32, yv);
         }
+      };
+      if constexpr (POST || !STAG) {
+#pragma unroll
+        for (int c = 0; c < CPS; ++c) {
+          const u32x4 yv = ycol(c);
+          if constexpr (kUnitStores) {
+            stage_col(0, phase, c, yv);
+            if constexpr (NEXT) load_col(tile + G, nlr, c);
+#pragma unroll
+            for (int u = 0; u < kUnits; ++u)
+              if (c == unit_done(u)) flush_unit(0, phase, u, ybw, off, wrows);
+          } else {
+            if (rok) st16_stream(yb + (uint32_t)((w * 16 + r16) * (int)D + q * 8) + c * 32, yv);
+            if constexpr (NEXT) load_col(tile + G, nlr, c);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < CPS; ++c) ystore(c, ycol(c));
+        if constexpr (NEXT) load_tile(tile + G);
       }
     }
   };
@@ -672,28 +848,41 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
 
 namespace {
 
+template <int NS, int CPS, bool POST, bool STAG>
+int occupancy_one() {
+  typedef ResShape<NS, CPS> F;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(pre_resident_kernel<NS, CPS, POST, STAG>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)F::lds_bytes) != hipSuccess)
+    return -1;
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, pre_resident_kernel<NS, CPS, POST, STAG>, kThreads,
+                                                   F::lds_bytes) != hipSuccess)
+    return -1;
+  return occ;
+}
+
+// Workgroups per CU of the (n, cps, layer boundary) tiling: the smaller of
+// its two kernels (with and without stagger), either of which may run.
 template <int NS, int CPS, bool POST>
 int occupancy_of() {
   typedef ResShape<NS, CPS> F;
   if constexpr (!(POST ? F::fits_post : F::fits)) {
     return 0;
   } else {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(pre_resident_kernel<NS, CPS, POST>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)F::lds_bytes) != hipSuccess)
-      return -1;
-    int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, pre_resident_kernel<NS, CPS, POST>, kThreads,
-                                                     F::lds_bytes) != hipSuccess)
-      return -1;
-    return occ;
+    const int a = occupancy_one<NS, CPS, POST, false>(), b = occupancy_one<NS, CPS, POST, true>();
+    return a < 0 || b < 0 ? -1 : (a < b ? a : b);
   }
 }
 
 template <int NS, int CPS, bool POST>
 void launch_one(const ResArgs& a, unsigned grid, hipStream_t s) {
   typedef ResShape<NS, CPS> F;
-  if constexpr (POST ? F::fits_post : F::fits)
-    hipLaunchKernelGGL((pre_resident_kernel<NS, CPS, POST>), dim3(grid), dim3(kThreads), F::lds_bytes, s, a);
+  if constexpr (POST ? F::fits_post : F::fits) {
+    if (a.stagger)
+      hipLaunchKernelGGL((pre_resident_kernel<NS, CPS, POST, true>), dim3(grid), dim3(kThreads), F::lds_bytes, s, a);
+    else
+      hipLaunchKernelGGL((pre_resident_kernel<NS, CPS, POST, false>), dim3(grid), dim3(kThreads), F::lds_bytes, s, a);
+  }
 }
 
 // Calls f.template operator()<NS, CPS>() for the runtime (n, cps).
@@ -831,15 +1020,18 @@ struct Launcher {
 };
 
 // Wall-clock ticks (100 MHz) an exchange wait lasts before it gives up: 100 ms,
-// or MHC_POLL_TICKS when that is set to a number >= 0. The variable is a test
-// hook: at 0 every wait not satisfied at its first read gives up, so the
-// time-out path runs while every kernel still exits normally.
+// or MHC_POLL_TICKS when that is set to a number >= -1. The variable is a test
+// hook: at 0 every wait not satisfied at its first read gives up, and at -1
+// the call publishes every exchanged word with a stale tag, so every wait
+// gives up at its first read (every token of the call is then lost and
+// written as NaN); the time-out path runs while every kernel still exits
+// normally.
 long long poll_ticks() {
   const char* e = std::getenv("MHC_POLL_TICKS");
   if (e && *e) {
     char* end = nullptr;
     const long long v = std::strtoll(e, &end, 10);
-    if (*end == '\0' && v >= 0) return v;
+    if (*end == '\0' && v >= -1) return v;
   }
   return kPollTicks;
 }
@@ -871,6 +1063,10 @@ ResArgs resident_args(const PrePlan& p, const void* residual, const float* fn, c
   a.eps = eps;
   a.K = (float)p.K;
   a.poll_ticks = poll_ticks();
+  const int64_t tiles = (p.T + kTM - 1) / kTM;
+  a.stagger = tiles >= (int64_t)kStaggerGenerations * p.rper ? 1 : 0;
+  // test hook: MHC_STAGGER = 1 or 0 forces the instance at any size
+  if (const char* e = std::getenv("MHC_STAGGER")) a.stagger = *e == '1' ? 1 : (*e == '0' ? 0 : a.stagger);
   return a;
 }
 }  // namespace

@@ -128,6 +128,21 @@ def test_boundary_fused(T, n, D):
         assert d <= (1e-2 if k == "y" else 1e-4), (k, d)
 
 
+@pytest.mark.parametrize("stagger", ["0", "1"])
+@pytest.mark.parametrize("T,n,D", [(300, 4, 2048), (67, 3, 1024), (2500, 4, 4096)], ids=lambda v: str(v))
+def test_boundary_both_pipelines(monkeypatch, T, n, D, stagger):
+    """Either instance of the single-pass kernel (MHC_STAGGER: workgroup-synchronous, or one pipeline per
+    wave) at the layer boundary, against the oracle on every token."""
+    monkeypatch.setenv("MHC_STAGGER", stagger)
+    x = W.generate(W.custom(T, n, D, "bf16", seed=T * 7 + n + D, fn_std=0.02))
+    g, post, comb, fn2 = _case(x)
+    ws = _workspace(x.spec, 0)
+    outs = _boundary(x, g, 0, ws)
+    assert mhc.mhc_pre_sync_timeouts(ws, g["residual"], 0) == 0
+    torch.cuda.synchronize()
+    _check_oracle(x, outs, post, comb, fn2, f"stagger {stagger} T{T} n{n} D{D}")
+
+
 @pytest.mark.parametrize("T,n,D,dt", FALLBACK, ids=lambda v: str(v))
 def test_boundary_fallback(T, n, D, dt):
     """Shapes the single-pass kernel does not cover run mhc_post's and mhc_pre's kernels in sequence."""

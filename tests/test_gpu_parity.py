@@ -416,40 +416,76 @@ def test_outputs_fully_written_and_bounded():
         assert torch.isnan(full[used:]).all()
 
 
-def test_exchange_time_out_is_reported_and_the_next_call_recovers(monkeypatch):
-    # The library's poll limit set to 0 ticks: every exchange wait that its first
-    # read does not satisfy gives up (a fresh workspace's grid barrier among
-    # them), so the call is marked timed out while every kernel exits normally.
+@pytest.mark.parametrize("stagger", ["0", "1"])
+def test_exchange_time_out_is_reported_and_the_next_call_recovers(monkeypatch, stagger):
+    # The library's poll limit is a test hook (every kernel still exits normally):
+    # at -1 every exchange wait gives up whatever it reads, so every token of the
+    # call is lost; at 0 every wait that its first read does not satisfy gives up
+    # (a fresh workspace's grid barrier among them). MHC_STAGGER picks the kernel
+    # instance: workgroup-synchronous (0) or one pipeline per wave (1).
+    monkeypatch.setenv("MHC_STAGGER", stagger)
     x = W.generate(W.custom(300, 4, 1024, "bf16", seed=11))
     g = _gpu_inputs(x)
     s = x.spec
+    op, oc, oy = _oracle_pre(x)
     need = mhc.mhc_pre_workspace_bytes(s.T, s.n, s.D, -1)
     ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
-    monkeypatch.setenv("MHC_POLL_TICKS", "0")
-    _say("  timed-out call (poll limit 0)")
-    post, comb, y = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], sinkhorn_repeat=s.sinkhorn_repeat,
-                                eps=s.eps, n_splits=-1, workspace=ws)
+
+    def call():
+        return mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], sinkhorn_repeat=s.sinkhorn_repeat,
+                           eps=s.eps, n_splits=-1, workspace=ws)
+
+    def lost_tokens(post, comb, y):
+        hp, hc, hy = host(post), host(comb), O.decode(host(y), "bf16")
+        return (np.isnan(hp).any(axis=1) | np.isnan(hc).reshape(s.T, -1).any(axis=1) | np.isnan(hy).any(axis=1),
+                hp, hc, host(y))
+
+    monkeypatch.setenv("MHC_POLL_TICKS", "-1")
+    _say("  every wait gives up (poll limit -1)")
+    out = call()
     assert mhc.mhc_pre_sync_timeouts(ws, g["residual"], -1) == 1
-    monkeypatch.delenv("MHC_POLL_TICKS")
-    # the call's outputs show it: a token whose exchange did not complete has NaN outputs, every other
-    # token is right
-    op, oc, oy = _oracle_pre(x)
-    hp, hc, hy = host(post), host(comb), O.decode(host(y), "bf16")
-    lost = np.isnan(hp).any(axis=1) | np.isnan(hc).reshape(s.T, -1).any(axis=1) | np.isnan(hy).any(axis=1)
-    _say(f"  timed-out call: {int(lost.sum())} of {s.T} tokens NaN")
-    assert lost.any(), "a timed-out call left no NaN output"
-    if (~lost).any():
+    lost, hp, hc, hy = lost_tokens(*out)
+    assert lost.all(), f"{int((~lost).sum())} tokens of a call whose every wait gave up are not NaN"
+    assert np.isnan(hp).all() and np.isnan(hc).all() and np.isnan(O.decode(hy, "bf16")).all()
+
+    monkeypatch.setenv("MHC_POLL_TICKS", "0")
+    _say("  waits give up after their first read (poll limit 0)")
+    out = call()
+    assert mhc.mhc_pre_sync_timeouts(ws, g["residual"], -1) == 1
+    lost, hp, hc, hy = lost_tokens(*out)
+    _say(f"  {int(lost.sum())} of {s.T} tokens NaN")
+    if (~lost).any():   # every token is NaN or right
         assert_close(hp[~lost], op[~lost], "gate", "post of completed tokens")
         assert_close(hc[~lost], oc[~lost], "gate", "comb of completed tokens")
-        assert_close(host(y)[~lost], oy[~lost], "tensor", "y of completed tokens")
+        assert_close(hy[~lost], oy[~lost], "tensor", "y of completed tokens")
+    monkeypatch.delenv("MHC_POLL_TICKS")
+
     # the next call on the same workspace is a normal one
-    post, comb, y = mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], sinkhorn_repeat=s.sinkhorn_repeat,
-                                eps=s.eps, n_splits=-1, workspace=ws)
+    post, comb, y = call()
     assert mhc.mhc_pre_sync_timeouts(ws, g["residual"], -1) == 0
-    op, oc, oy = _oracle_pre(x)
     assert_close(host(post), op, "gate", "post after a timed-out call")
     assert_close(host(comb), oc, "gate", "comb after a timed-out call")
     assert_close(host(y), oy, "tensor", "y after a timed-out call")
+
+
+PIPELINE_CASES = [
+    # (T, n, D): ragged tails, every n of the single-pass path, several generations
+    (300, 4, 7168), (129, 3, 2240), (1000, 2, 512), (17, 1, 2048), (2500, 4, 4096),
+]
+
+
+@pytest.mark.parametrize("stagger", ["0", "1"])
+@pytest.mark.parametrize("T,n,D", PIPELINE_CASES, ids=lambda v: str(v))
+def test_both_pipelines(monkeypatch, T, n, D, stagger):
+    """The single-pass kernel has two instances, chosen by the number of generations: the workgroup
+    finalises its tile's tokens together, or (from four generations on) every wave runs its own pipeline
+    and finalises its own tokens. MHC_STAGGER forces either at any size; both must match the oracle."""
+    monkeypatch.setenv("MHC_STAGGER", stagger)
+    x = W.generate(W.custom(T, n, D, "bf16", seed=T + n + D, fn_std=0.05 if n < 4 else 0.02))
+    g = _gpu_inputs(x)
+    tokens = None if T <= 1000 else np.unique(np.concatenate([[0, T - 1], np.arange(T - 130, T),
+                                                             np.random.default_rng(3).choice(T, 64, replace=False)]))
+    _check_pre(x, g, -1, tokens, f"stagger {stagger} T{T} n{n} D{D}")
 
 
 def test_side_stream_without_workspace():
