@@ -55,7 +55,16 @@ typedef enum {
   MHC_ERR_HIP = -5           /* a HIP launch failed */
 } mhc_status;
 
-typedef enum { MHC_BF16 = 0, MHC_F32 = 1 } mhc_dtype;
+/* Element type of residual, h, y and out. The two range markers make the
+ * type span every int (C++ gives an enum only the values its enumerators'
+ * bits cover), so a caller's out-of-range value is well defined and is
+ * rejected with MHC_ERR_INVALID_ARG; they are not element types. */
+typedef enum {
+  MHC_BF16 = 0,
+  MHC_F32 = 1,
+  MHC_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  MHC_DTYPE_RANGE_MAX_ = 2147483647
+} mhc_dtype;
 
 /* Human-readable name of a status code (static string, never NULL). */
 MHC_API const char* mhc_status_string(int status);

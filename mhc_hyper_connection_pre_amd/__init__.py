@@ -58,6 +58,12 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run `python -m mhc_hyper_connection_pre_amd.build` "
                            "(there is no CPU fallback)")
+    _LIB = load_library(path)
+    return _LIB
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """Load a build of the C ABI at `path` and declare its signatures (``lib()`` loads the in-tree one)."""
     L = ctypes.CDLL(path)
     P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     L.mhc_status_string.argtypes = [I]
@@ -82,7 +88,6 @@ def lib() -> ctypes.CDLL:
     L.mhc_post_pre.restype = I
     L.mhc_post_pre_fused.argtypes = [I64, I, I64, I, I]
     L.mhc_post_pre_fused.restype = I
-    _LIB = L
     return L
 
 

@@ -76,5 +76,51 @@ def build_library(verbose: bool = False, jobs: int = 8) -> str:
     return LIB
 
 
+HOST_SOURCES = [s for s in SOURCES if s.endswith(".cpp")]
+HOSTSAN_LIB = os.path.join(OBJDIR, "libmhc_hostsan.so")
+
+
+def build_hostsan_library(verbose: bool = False) -> str:
+    """A build of the C ABI whose host-only sources (argument checks, plans,
+    the tile table) carry AddressSanitizer and UndefinedBehaviorSanitizer,
+    linked with the kernels' objects of the last ``build_library()`` (device
+    code is not instrumented). Loading it needs the sanitizer runtime first in
+    the process (LD_PRELOAD of ``sanitizer_runtime()``). Returns its path."""
+    cc = hipcc()
+    objs = []
+    for src in HOST_SOURCES:
+        obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".hostsan.o")
+        objs.append(obj)
+        cmd = [cc, "-O1", "-g", "-fno-omit-frame-pointer", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"-I{INCLUDE}",
+               "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+               "-Xarch_host", "-fno-sanitize-recover=undefined", "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}")
+    for src in SOURCES:
+        if not src.endswith(".cpp"):
+            obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
+            if not os.path.exists(obj):
+                raise RuntimeError(f"{obj} is missing; run build_library() first")
+            objs.append(obj)
+    link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-Xarch_host", "-fsanitize=address",
+            "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", "-o", HOSTSAN_LIB]
+    r = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}")
+    return HOSTSAN_LIB
+
+
+def sanitizer_runtime() -> str:
+    """Path of the shared AddressSanitizer runtime of the ROCm compiler."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "lib", "llvm", "bin", "clang++")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang++"
+    out = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return out.stdout.strip()
+
+
 if __name__ == "__main__":
     print(build_library(verbose="-v" in sys.argv))

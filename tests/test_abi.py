@@ -25,6 +25,11 @@ def declared_symbols():
 
 @pytest.fixture(scope="module")
 def L():
+    # MHC_ABI_LIBRARY: another build of the same sources to run these checks on
+    # (the host-sanitizer build of test_abi_hostsan.py)
+    other = os.environ.get("MHC_ABI_LIBRARY")
+    if other:
+        return mhc.load_library(other)
     if not os.path.exists(mhc.library_path()):
         pytest.skip("libmhc.so not built")
     return mhc.lib()
@@ -96,6 +101,25 @@ def test_pre_validation(L):
     assert pre(L, y=A + 0x60000 - 0x7f0) == INVALID         # y runs into bias
     assert pre(L, post=A + 0x100000 + 0x200) == INVALID     # post inside the workspace
     assert pre(L, ws=A + 0x10000 + 0x300, ws_bytes=need) == INVALID   # workspace over the end of comb
+
+
+HUGE = [(2**62, 4, 64), (16, 4, 2**60), (2**40, 4, 2**40), (2**63 - 1, 1, 8), (16, 4, 2**63 - 8),
+        (2**31, 4, 7168), (1, 2**31 - 1, 8)]
+
+
+@pytest.mark.parametrize("T,n,D", HUGE, ids=str)
+def test_sizes_near_the_integer_limits_are_refused(L, T, n, D):
+    """Element counts that overflow 64 bits, or pass the 32-bit lane offsets the kernels use, are refused
+    before any arithmetic on them can overflow (the host-sanitizer build runs these too)."""
+    assert pre(L, T=T, n=n, D=D) == UNSUPPORTED
+    assert L.mhc_pre_workspace_bytes(T, n, D, 0, BF16) == 0
+    assert L.mhc_pre_splits(T, n, D, 0, BF16) == UNSUPPORTED
+    assert L.mhc_post_pre_fused(T, n, D, 0, BF16) == UNSUPPORTED
+    assert L.mhc_post(A, A + 0x10000, A + 0x20000, A + 0x30000, A + 0x40000, BF16, T, n, D, None) < 0
+    assert L.mhc_post_combine_norm(A, None, A + 0x10000, A + 0x20000, A + 0x30000, A + 0x40000, A + 0x50000,
+                                   A + 0x60000, 1e-6, BF16, T, n, D, None) < 0
+    assert L.mhc_pre_splits(16, 4, 64, -2**31, BF16) == INVALID
+    assert L.mhc_pre_splits(16, 4, 64, 2**31 - 1, BF16) == INVALID
 
 
 def test_pre_static_validation(L):
