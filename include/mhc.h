@@ -109,7 +109,7 @@ MHC_API size_t mhc_pre_workspace_bytes(int64_t T, int n, int64_t D, int n_splits
  *   hidden axis: 0 = library choice; 1..256 = that many partials on the
  *   two-pass path; -1 = the single-pass path with the library's tiling, -S
  *   (2 <= S <= 256) = the single-pass path with S slices of the hidden axis
- *   (D = 32 * cps * S with cps one of 1, 2, 4, 5, 7, 8, 14), or an error for
+ *   (D = 32 * cps * S with cps one of 1 to 8 or 14), or an error for
  *   either (MHC_ERR_UNSUPPORTED for a shape or slice count it does not cover,
  *   MHC_ERR_MISALIGNED for an fn that is not 16-byte aligned); tile tables
  *   and tuners choose among these values. Any value gives the same result

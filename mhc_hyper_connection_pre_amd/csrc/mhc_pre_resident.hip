@@ -77,7 +77,7 @@ constexpr int kMaxAVgprs = 128;           // residual registers per wave
 constexpr int kMaxAVgprsPost = 144;       // residual + block-output registers (layer boundary)
 constexpr int kLdsMax = 160 * 1024;
 constexpr long long kPollTicks = 10000000LL;  // 100 ms of the 100 MHz wall clock
-constexpr int kCpsList[] = {1, 2, 4, 5, 7, 8, 14};
+constexpr int kCpsList[] = {1, 2, 3, 4, 5, 6, 7, 8, 14};
 constexpr int kStaggerGenerations = 4;    // from this many generations on, waves run their own pipelines
 
 typedef unsigned long long u64;
@@ -597,7 +597,10 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
     // half = lane / 32) sums column c over slices half, half + 2, ... in order,
     // the two halves are added, and lanes 0..15 run the epilogue of the token.
     if constexpr (STAG) {
-      constexpr int kFW = CPS >= 4 ? 16 : 40;   // partial words per lane and round
+      // partial words per lane and round: 32 slices per round trip (more
+      // slices come from narrow tilings, which run this instance only when
+      // forced; 40 words made such instances spill)
+      constexpr int kFW = 16;
       const int S = a.S;
       int r = (sg - 16 * w) % S;
       if (r < 0) r += S;
@@ -892,8 +895,10 @@ auto dispatch(int n, int cps, Fn&& f) {
   switch (cps) {                                        \
     case 1: return f.template operator()<NS, 1>();      \
     case 2: return f.template operator()<NS, 2>();      \
+    case 3: return f.template operator()<NS, 3>();      \
     case 4: return f.template operator()<NS, 4>();      \
     case 5: return f.template operator()<NS, 5>();      \
+    case 6: return f.template operator()<NS, 6>();      \
     case 7: return f.template operator()<NS, 7>();      \
     case 8: return f.template operator()<NS, 8>();      \
     default: return f.template operator()<NS, 14>();    \

@@ -38,7 +38,7 @@ import sys
 
 import mhc_hyper_connection_pre_amd as mhc
 
-DEFAULT_SHAPES = ["4,4096", "4,5120", "4,7168", "8,4096", "8,7168"]
+DEFAULT_SHAPES = ["2,4096", "2,7168", "3,3072", "4,4096", "4,5120", "4,6144", "4,7168", "8,4096", "8,7168"]
 DEFAULT_TOKENS = [16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384]
 TWO_PASS_SPLITS = [1, 2, 4, 8, 16, 32, 64]
 KEEP_LIBRARY_WITHIN = 1.03

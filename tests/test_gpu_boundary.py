@@ -129,7 +129,8 @@ def test_boundary_fused(T, n, D):
 
 
 @pytest.mark.parametrize("stagger", ["0", "1"])
-@pytest.mark.parametrize("T,n,D", [(300, 4, 2048), (67, 3, 1024), (2500, 4, 4096)], ids=lambda v: str(v))
+@pytest.mark.parametrize("T,n,D", [(300, 4, 2048), (67, 3, 1024), (2500, 4, 4096), (300, 4, 6144), (700, 3, 3072)],
+                         ids=lambda v: str(v))
 def test_boundary_both_pipelines(monkeypatch, T, n, D, stagger):
     """Either instance of the single-pass kernel (MHC_STAGGER: workgroup-synchronous, or one pipeline per
     wave) at the layer boundary, against the oracle on every token."""

@@ -471,6 +471,8 @@ def test_exchange_time_out_is_reported_and_the_next_call_recovers(monkeypatch, s
 PIPELINE_CASES = [
     # (T, n, D): ragged tails, every n of the single-pass path, several generations
     (300, 4, 7168), (129, 3, 2240), (1000, 2, 512), (17, 1, 2048), (2500, 4, 4096),
+    # three and six columns per slice (D = 3072 and 6144 at 32 slices)
+    (700, 3, 3072), (300, 4, 6144), (2048, 4, 6144),
 ]
 
 

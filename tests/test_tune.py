@@ -51,6 +51,9 @@ def test_committed_table_matches_its_record():
     if not os.path.exists(rec):
         pytest.skip("no tuner record")
     d = json.load(open(rec))
+    # the record covers n = 2, 3, 4 and 8, and several hidden sizes at n = 4
+    assert {e["n"] for e in d["entries"]} >= {2, 3, 4, 8}
+    assert {e["D"] for e in d["entries"] if e["n"] == 4} >= {4096, 5120, 6144, 7168}
     with open(os.path.join(build.CSRC, "mhc_tile_table.cpp")) as f:
         text = f.read()
     assert d["measured"] in text
