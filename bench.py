@@ -250,7 +250,14 @@ def revision_info():
                     h.update(name.encode() + b"\0" + f.read())
     with open(os.path.abspath(__file__), "rb") as f:
         h.update(b"bench.py\0" + f.read())
-    return {"git": rev, "sources_sha256_16": h.hexdigest()[:16]}
+    out = {"git": rev, "sources_sha256_16": h.hexdigest()[:16]}
+    # the revision the library was built from, recorded by the build beside it
+    path = os.path.join(ROOT, "mhc_hyper_connection_pre_amd", "libmhc.revision")
+    if os.path.exists(path):
+        vals = dict(line.split(": ", 1) for line in open(path).read().splitlines() if ": " in line)
+        out["library_built_from_git"] = None if vals.get("git") in (None, "None") else vals["git"]
+        out["library_tree_had_uncommitted_changes"] = {"True": True, "False": False}.get(vals.get("dirty"))
+    return out
 
 
 # ---------------------------------------------------------------- timing events

@@ -73,7 +73,28 @@ def build_library(verbose: bool = False, jobs: int = 8) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}")
     os.replace(tmp, LIB)
+    _write_revision()
     return LIB
+
+
+REVISION_FILE = os.path.join(PKG, "libmhc.revision")
+
+
+def _write_revision() -> None:
+    """Record beside the library the git revision of the tree it was built from (and whether the tree had
+    uncommitted changes), for copies of the tree that travel without their history."""
+    rev, dirty = None, None
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=10)
+        if r.returncode == 0:
+            rev = r.stdout.strip() or None
+            d = subprocess.run(["git", "-C", ROOT, "status", "--porcelain", "--untracked-files=no"],
+                               capture_output=True, text=True, timeout=10)
+            dirty = bool(d.stdout.strip()) if d.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError):
+        pass
+    with open(REVISION_FILE, "w") as f:
+        f.write(f"git: {rev}\ndirty: {dirty}\n")
 
 
 HOST_SOURCES = [s for s in SOURCES if s.endswith(".cpp")]
