@@ -217,8 +217,11 @@ def test_boundary_shares_workspace_with_pre():
             assert_close(host(got), want, kind, f"pre round {k} {name}")
 
 
-def test_boundary_graph_replay():
-    """Captured once, replayed three times with eager calls on the same workspace in between."""
+@pytest.mark.parametrize("stagger", ["0", "1"])
+def test_boundary_graph_replay(monkeypatch, stagger):
+    """Captured once, replayed three times with eager calls on the same workspace in between; either kernel
+    instance (MHC_STAGGER is read when the call is captured)."""
+    monkeypatch.setenv("MHC_STAGGER", stagger)
     x = W.generate(W.custom(257, 4, 1024, "bf16", seed=66, fn_std=0.02))
     g, post, comb, fn2 = _case(x)
     s = x.spec
