@@ -250,7 +250,8 @@ MHC_API int mhc_post_pre_fused(int64_t T, int n, int64_t D, int n_splits, mhc_dt
  *   NULL to skip writing it). They must not overlap each other or an input
  *   (MHC_ERR_INVALID_ARG).
  * Inputs: as mhc_post, plus combine_w float32 [T, n] and norm_weight float32
- *   [D]; norm_eps > 0. D <= 32768 (bf16) or 16384 (f32).
+ *   [D]; norm_eps > 0. D <= 32768 (bf16) or 16384 (f32); at n = 8,
+ *   D <= 16384 (bf16) or 8192 (f32).
  */
 MHC_API int mhc_post_combine_norm(void* normalized, void* out_residual,
                                   const void* h, const void* residual,

@@ -353,7 +353,7 @@ MHC_API int mhc_post_combine_norm(void* normalized, void* out_residual, const vo
   int st = check_shape(T, n, D, dt);
   if (st != MHC_OK) return st;
   if (!(norm_eps > 0.0f) || !std::isfinite(norm_eps)) return MHC_ERR_INVALID_ARG;
-  if (D / vec_elems(dt) > kPcnMaxVectors) return MHC_ERR_UNSUPPORTED;
+  if (D / vec_elems(dt) > pcn_max_vectors(n)) return MHC_ERR_UNSUPPORTED;
   if (T == 0) return MHC_OK;
   if (!normalized || !h || !residual || !post || !comb || !combine_w || !norm_weight) return MHC_ERR_INVALID_ARG;
   if (!aligned(normalized, 16) || !aligned(h, 16) || !aligned(residual, 16) ||

@@ -108,7 +108,10 @@ int pre_call(float* post, float* comb, void* y, const void* residual, mhc_dtype 
              const float* hc_scale, const float* bias, int64_t T, int n, int64_t D, int sinkhorn_repeat, float eps,
              int n_splits, void* workspace, size_t workspace_bytes, hipStream_t s, WorkspaceProvider provider);
 
-// Largest D the fused combine+norm kernel keeps in registers: 1024 threads x 4 vectors.
-constexpr int64_t kPcnMaxVectors = 1024 * 4;
+// Threads per workgroup of the fused combine+norm kernel, and the longest row
+// (in 16-byte vectors) it keeps in registers: threads x 4 vectors.
+template <int NS>
+constexpr int kPcnThreads = NS > 4 ? 512 : 1024;
+constexpr int64_t pcn_max_vectors(int n) { return n > 4 ? 512 * 4 : 1024 * 4; }
 
 }  // namespace mhc

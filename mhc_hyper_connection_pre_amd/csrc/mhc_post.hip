@@ -19,10 +19,11 @@
 
 namespace mhc {
 
-constexpr int kPostThreads = 256;
+constexpr int kPostMaxThreads = 1024;   // rows of up to 1024 vectors: one vector per thread
+constexpr int kPostWideThreads = 256;   // longer rows: up to four vectors per thread and round
 
 template <class S, int NS, int CPT>
-__global__ __launch_bounds__(kPostThreads) void post_kernel(typename S::elem* __restrict__ out,
+__global__ __launch_bounds__(CPT == 1 ? kPostMaxThreads : kPostWideThreads) void post_kernel(typename S::elem* __restrict__ out,
                                                             const typename S::elem* __restrict__ h,
                                                             const typename S::elem* __restrict__ x,
                                                             const float* __restrict__ post,
@@ -42,11 +43,12 @@ __global__ __launch_bounds__(kPostThreads) void post_kernel(typename S::elem* __
   const typename S::elem* xt = x + t * NS * D;
   typename S::elem* ot = out + t * NS * D;
 
-  for (int64_t base = 0; base < nch; base += (int64_t)kPostThreads * CPT) {
+  const int nthr = blockDim.x;
+  for (int64_t base = 0; base < nch; base += (int64_t)nthr * CPT) {
     u32x4 hv[CPT], xv[CPT][NS];
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
-      const int64_t c = base + tid + (int64_t)k * kPostThreads;
+      const int64_t c = base + tid + (int64_t)k * nthr;
       if (c < nch) {   // streaming loads: nothing of h or the residual is read twice here
         hv[k] = ld16_stream(ht + c * V);
 #pragma unroll
@@ -55,7 +57,7 @@ __global__ __launch_bounds__(kPostThreads) void post_kernel(typename S::elem* __
     }
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
-      const int64_t c = base + tid + (int64_t)k * kPostThreads;
+      const int64_t c = base + tid + (int64_t)k * nthr;
       if (c >= nch) continue;
       float hf[V], xf[NS][V];
       Vec<S>::unpack(hv[k], hf);
@@ -83,9 +85,20 @@ static hipError_t launch_post_n(const void* h, const void* residual, const float
   typedef typename S::elem E;
   const int64_t nch = D / S::V;
   constexpr int kMaxCpt = NS > 4 ? 2 : 4;   // vectors in flight per thread: (n + 1) x CPT x 4 registers
-  int cpt = (int)((nch + kPostThreads - 1) / kPostThreads);
-  cpt = cpt < 1 ? 1 : (cpt > kMaxCpt ? kMaxCpt : cpt);
-  const dim3 grid((unsigned)T), block(kPostThreads);
+  // one thread per 16-byte vector of the row, in whole waves, up to 1024:
+  // at D = 7168 (896 threads, one vector of h and of each stream per thread)
+  // this measured 48.5 us per call after a cache sweep against 52.4 us with
+  // 256 threads holding four vectors each (T = 2048, n = 4), 354 against
+  // 377 us at T = 16384; more waves per CU issue the same bytes sooner
+  // (rows longer than 1024 vectors keep 256 threads with up to kMaxCpt
+  // vectors each, within the registers that block size leaves)
+  int threads = (int)((nch + 63) / 64 * 64), cpt = 1;
+  if (nch > kPostMaxThreads) {
+    threads = kPostWideThreads;
+    cpt = (int)((nch + threads - 1) / threads);
+    cpt = cpt < 2 ? 2 : (cpt > kMaxCpt ? kMaxCpt : cpt);
+  }
+  const dim3 grid((unsigned)T), block(threads);
   E* o = static_cast<E*>(out);
   const E* hh = static_cast<const E*>(h);
   const E* x = static_cast<const E*>(residual);
@@ -124,12 +137,13 @@ hipError_t launch_post(const void* h, const void* residual, const float* post, c
 }
 
 // ------------------------------------------------------------------ fused post + combine + RMSNorm
-// One workgroup of up to 1024 threads per token; each thread keeps at most
-// CPT vectors of the combined row in registers (stored values, already
-// rounded), so the row is read from HBM once. The sum of squares is reduced
-// across the workgroup in a fixed order (wave butterfly, then LDS).
+// One workgroup of up to 1024 threads per token (512 at n = 8, whose eight
+// streams per vector need the registers of two waves per SIMD); each thread
+// keeps at most CPT vectors of the combined row in registers (stored values,
+// already rounded), so the row is read from HBM once. The sum of squares is
+// reduced across the workgroup in a fixed order (wave butterfly, then LDS).
 template <class S, int NS, int CPT>
-__global__ __launch_bounds__(1024) void post_combine_norm_kernel(
+__global__ __launch_bounds__(kPcnThreads<NS>) void post_combine_norm_kernel(
     typename S::elem* __restrict__ normalized, typename S::elem* __restrict__ out,
     const typename S::elem* __restrict__ h, const typename S::elem* __restrict__ x, const float* __restrict__ post,
     const float* __restrict__ comb, const float* __restrict__ combine_w, const float* __restrict__ norm_weight,
@@ -224,7 +238,7 @@ static hipError_t launch_pcn_n(void* normalized, void* out, const void* h, const
   typedef typename S::elem E;
   const int64_t nch = D / S::V;
   int64_t thr = ((nch + 63) / 64) * 64;
-  if (thr > 1024) thr = 1024;
+  if (thr > kPcnThreads<NS>) thr = kPcnThreads<NS>;
   const int cpt = (int)((nch + thr - 1) / thr);
   const dim3 grid((unsigned)T), block((unsigned)thr);
   E* nz = static_cast<E*>(normalized);

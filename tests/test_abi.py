@@ -264,6 +264,9 @@ def test_post_combine_norm_validation(L):
     assert pcn(nz=A + 0x70000 + 0x80) == INVALID   # normalized over norm_weight
     assert pcn(D=8 * 4097) == UNSUPPORTED          # more than 1024 threads x 4 vectors
     assert pcn(D=8 * 4096, T=0) == OK
+    assert pcn(n=8, D=8 * 2049) == UNSUPPORTED     # n = 8: 512 threads x 4 vectors
+    assert pcn(n=8, D=8 * 2048, T=0) == OK
+    assert pcn(n=8, D=4 * 2049, dt=F32) == UNSUPPORTED
 
 
 def test_binding_raises_without_gpu_tensors(L):
