@@ -64,6 +64,29 @@ def assert_close(got, want, kind, what):
 U32 = 2.0 ** -24   # unit roundoff of fp32
 
 
+def assert_y_f32(got, want64, pre64, x64, what):
+    """fp32 y = sum_i pre_i x_i against the oracle's float64 y, within the gate tolerance carried through
+    the stream sum: |got - y| <= (TOL_F32 + 4 (n + 1) u) * sum_i pre_i |x_i| for every element.
+
+    The pages fix a tolerance for bf16 outputs and for the fp32 gates only. A y whose pre gates each lie
+    within the gates' 1e-3 of the oracle's differs from it by at most 1e-3 * sum_i pre_i |x_i|, plus the
+    fp32 rounding of the (n + 1)-term result; the fp32 mixing GEMM over K = n D terms moves the gates by
+    about K u relative to the terms, so near elements where the streams cancel, y's difference is not
+    small next to y itself (the floored metric then reads above 1e-3 once K passes ~10^4).
+    pre64 [T, n] and x64 [T, n, D] are the oracle's gate and the decoded residual; returns the largest
+    ratio of the difference to that bound (<= 1)."""
+    g = np.asarray(got, dtype=np.float64)
+    w = np.asarray(want64, dtype=np.float64)
+    n = pre64.shape[1]
+    scale = np.einsum("ti,tid->td", np.abs(pre64), np.abs(x64))
+    bound = (TOL_F32 + 4 * (n + 1) * U32) * scale
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    ratio = np.abs(g - w) / np.maximum(bound, 1e-300)
+    worst = float(np.max(ratio)) if ratio.size else 0.0
+    assert worst <= 1.0, f"{what}: difference {worst:.3f} x the propagated gate bound"
+    return worst
+
+
 def ulp(v, dtype):
     """Spacing of the storage format at |v| (one step up at the top of a binade, so a neighbour above is
     covered); dtype 'bf16' or 'f32'."""
