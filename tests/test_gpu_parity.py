@@ -518,6 +518,39 @@ def test_side_stream_without_workspace():
                      "tensor", f"side stream {k} out")
 
 
+def test_two_streams_with_their_own_workspaces():
+    """Two single-pass calls in flight at once on two streams, each with its own workspace, sized so that
+    both grids fit on the chip together (80 + 64 workgroups): neither waits for the other, and each meets
+    the oracle (the exchange words of one call never reach the other's workspace)."""
+    xa = W.generate(W.custom(64, 4, 5120, "bf16", seed=41, fn_std=0.02))
+    xb = W.generate(W.custom(100, 3, 2048, "bf16", seed=42, fn_std=0.05))
+    cases = []
+    for x in (xa, xb):
+        s = x.spec
+        need = mhc.mhc_pre_workspace_bytes(s.T, s.n, s.D, -1)
+        assert mhc.mhc_pre_splits(s.T, s.n, s.D, -1) * ((s.T + 127) // 128) <= 128
+        cases.append((x, _gpu_inputs(x), torch.zeros(need, dtype=torch.uint8, device="cuda")))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for k in range(3):
+        for (x, g, ws), st in zip(cases, streams):
+            s = x.spec
+            outs.append(mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], n_splits=-1, workspace=ws,
+                                    stream=st))
+    for st in streams:
+        st.synchronize()
+    for k, (p, c, y) in enumerate(outs):
+        x, g, ws = cases[k % 2]
+        op, oc, oy = _oracle_pre(x)
+        assert_close(host(p), op, "gate", f"stream {k % 2} call {k // 2} post")
+        assert_close(host(c), oc, "gate", f"stream {k % 2} call {k // 2} comb")
+        assert_close(host(y), oy, "tensor", f"stream {k % 2} call {k // 2} y")
+    for x, g, ws in cases:
+        assert mhc.mhc_pre_sync_timeouts(ws, g["residual"], -1) == 0
+
+
 def test_prepared_calls_repeat_the_direct_calls():
     # A PreparedCall checks and marshals once; each call launches the same entry point with the same
     # arguments, so its outputs are the direct call's bits, call after call.
