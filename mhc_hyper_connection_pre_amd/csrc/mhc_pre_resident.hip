@@ -565,33 +565,47 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
       }
     }
     if constexpr (!STAG) __syncthreads();   // every wave has published before any finalises
-    // layer boundary: out goes to HBM now, while the tile's exchange below
-    // leaves HBM mostly idle (stored during the GEMM it competed with the
-    // residual loads: 8 us more per call at T = 2048, n = 4, D = 7168)
-    if constexpr (POST && kUnitStores) {
-      const int64_t wrow0 = (int64_t)tile * kTM + w * 16;
-      const int wrows = T - wrow0 < 16 ? (int)(T - wrow0) : 16;
-      uint16_t* obw = ob + (uint32_t)(w * 16 * NS * (int)D);
-      const uint32_t off[2] = {(uint32_t)((lane >> 3) * NS * (int)D + (lane & 7) * 8),
-                               (uint32_t)((8 + (lane >> 3)) * NS * (int)D + (lane & 7) * 8)};
-      const int phase = (int)(d0 >> 5) & 1;   // as every stream when D is a multiple of 64
+    // layer boundary: out goes to HBM from here on, while the tile's exchange
+    // below leaves HBM mostly idle (stored during the GEMM it competed with
+    // the residual loads: 8 us more per call at T = 2048, n = 4, D = 7168).
+    // store_out(J0, J1) stores streams J0 .. J1 - 1 of this wave's rows.
+    auto store_out = [&](auto j0_tag, auto j1_tag) {
+      constexpr int J0 = decltype(j0_tag)::value, J1 = decltype(j1_tag)::value;
+      if constexpr (POST && kUnitStores) {
+        const int64_t wrow0 = (int64_t)tile * kTM + w * 16;
+        const int wrows = T - wrow0 < 16 ? (int)(T - wrow0) : 16;
+        uint16_t* obw = ob + (uint32_t)(w * 16 * NS * (int)D);
+        const uint32_t off[2] = {(uint32_t)((lane >> 3) * NS * (int)D + (lane & 7) * 8),
+                                 (uint32_t)((8 + (lane >> 3)) * NS * (int)D + (lane & 7) * 8)};
+        const int phase = (int)(d0 >> 5) & 1;   // as every stream when D is a multiple of 64
 #pragma unroll
-      for (int jj = 0; jj < NS; ++jj) {
+        for (int jj = J0; jj < J1; ++jj) {
 #pragma unroll
-        for (int c = 0; c < CPS; ++c) {
-          stage_col(jj * kUnits, phase, c, A[jj * CPS + c]);
+          for (int c = 0; c < CPS; ++c) {
+            stage_col(jj * kUnits, phase, c, A[jj * CPS + c]);
 #pragma unroll
-          for (int u = 0; u < kUnits; ++u)
-            if (c == unit_done(u)) flush_unit(jj * kUnits, phase, u, obw + jj * D, off, wrows);
+            for (int u = 0; u < kUnits; ++u)
+              if (c == unit_done(u)) flush_unit(jj * kUnits, phase, u, obw + jj * D, off, wrows);
+          }
         }
+      } else if constexpr (POST) {
+#pragma unroll
+        for (int c = 0; c < CPS; ++c)
+#pragma unroll
+          for (int jj = J0; jj < J1; ++jj)
+            if (rok) st16_stream(ob + jj * D + oo + c * 32, A[jj * CPS + c]);
       }
-    } else if constexpr (POST) {
-#pragma unroll
-      for (int c = 0; c < CPS; ++c)
-#pragma unroll
-        for (int jj = 0; jj < NS; ++jj)
-          if (rok) st16_stream(ob + jj * D + oo + c * 32, A[jj * CPS + c]);
-    }
+    };
+    // The first half of the streams goes out here, the second once this
+    // workgroup's (or wave's) finalising reads have returned: on gfx950 the
+    // vector memory counter is shared by loads and stores and drains in issue
+    // order, so a poll issued behind every out store would wait for all of
+    // them. Measured per call after a cache sweep (n = 4): 83.9 -> 82.8 us at
+    // T = 2048, D = 7168; 54.3 -> 52.8 us at D = 4096; 17.0 -> 15.9 us at
+    // T = 64, D = 5120; 583 -> 579 us at T = 16384 (all streams after the
+    // finalise instead: 103 us at T = 2048; all after the pre poll: 88.7 us).
+    constexpr int kOutSplit = NS / 2;
+    store_out(std::integral_constant<int, 0>{}, std::integral_constant<int, kOutSplit>{});
     // ---- 3. finalise the tile's tokens sg, sg + S, ... . With stagger, each
     // wave finalises those in its own 16 rows: lane (column c = lane % 32,
     // half = lane / 32) sums column c over slices half, half + 2, ... in order,
@@ -660,6 +674,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
           if (act) a.comb[tok * NS * NS + (lane >> 2) * NS + (lane & 3)] = combv;
         }
       }
+      store_out(std::integral_constant<int, kOutSplit>{}, std::integral_constant<int, NS>{});
     } else {
       // Without stagger the workgroup finalises them together, TB at a time.
       // Thread (c = tid % 32, group = tid / 32) sums column c of splits sub,
@@ -704,7 +719,6 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
             ready = ready && tag_is(vv[u], tag);
             accm += tag_val(vv[u]);
           }
-          
           // The whole workgroup leaves at the same iteration, once every thread
           // has its words or has run out of time (each wave reads the clock on
           // its own, so the decision goes through the barrier's reduction).
@@ -713,6 +727,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
           __builtin_amdgcn_s_sleep(1);
         }
         gs[(mm * SUBS + sub) * 32 + c] = accm;
+        if (m0 == 0) store_out(std::integral_constant<int, kOutSplit>{}, std::integral_constant<int, NS>{});
         // a batch with a word still missing is lost: its tokens get NaN gates
         // and comb (and through pre, NaN y), so the call's outputs show it
         const bool lost = __syncthreads_or(!ready);
@@ -745,6 +760,11 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
       }
     }
 
+    if constexpr (!STAG) {
+      // workgroups that finalise no token of this tile
+      if (sg >= (T - (int64_t)tile * kTM < kTM ? (int)(T - (int64_t)tile * kTM) : kTM))
+        store_out(std::integral_constant<int, kOutSplit>{}, std::integral_constant<int, NS>{});
+    }
     // ---- 4. pre of this wave's 16 tokens (polled), then y for the slice
     float pre[NS];
     {
