@@ -180,6 +180,11 @@ def test_pre_plan(L):
     assert L.mhc_pre_splits(T, n, D, -16, BF16) == UNSUPPORTED       # cps 14: its residual slice needs too many registers
     assert L.mhc_pre_splits(T, n, D, -28, BF16) == UNSUPPORTED       # cps 8: its fn fragments do not fit in LDS
     assert L.mhc_pre_splits(T, n, D, -2, BF16) == UNSUPPORTED        # cps 112 is not built
+    # slices of three and six columns: D = 3072 and 6144 take 32 slices (two generations at T = 2048)
+    assert L.mhc_pre_splits(T, 4, 6144, -1, BF16) == 32
+    assert L.mhc_pre_splits(T, 3, 3072, -32, BF16) == 32
+    assert L.mhc_pre_splits(T, 4, 6144, -48, BF16) == 48               # cps 4 still accepted
+    assert L.mhc_post_pre_fused(T, 4, 6144, -32, BF16) == 1           # 4 n cps + 4 cps = 120 registers
     assert L.mhc_pre_splits(T, n, 104, -1, F32) == UNSUPPORTED
     # fp32 residuals always take the two-pass path (no packed fn)
     assert L.mhc_pre_workspace_bytes(8, 4, 256, 0, F32) == 256 + (L.mhc_pre_splits(8, 4, 256, 0, F32) * 8 * 28 * 4 + 255) // 256 * 256
