@@ -3,7 +3,8 @@
 The named workloads and the targeted cases fix one axis at a time; this sweep
 draws all of them at once (n, D, T, dtype, n_splits among the values the
 library accepts for the shape, the single-pass kernel's instance, hc_scale,
-sinkhorn_repeat, eps), for the pre step and for the layer boundary, so that a
+sinkhorn_repeat, eps), for the pre step (also in long runs of generations,
+T up to 8192) and for the layer boundary, so that a
 combination no targeted case covers still meets the oracle. The draws are
 fixed by the seed: a failure names its case and reproduces.
 """
@@ -69,6 +70,26 @@ PRE_CASES = _draw(96, boundary=False)
 BOUNDARY_CASES = _draw(32, boundary=True)
 
 
+def _draw_long(count):
+    """Long runs of generations on the single-pass kernel: bf16, n <= 4, T up to 8192."""
+    rng = np.random.default_rng(SEED + 2)
+    out = []
+    while len(out) < count:
+        n = int(rng.choice([2, 3, 4, 4]))
+        D = int(32 * rng.integers(8, 225))
+        T = int(rng.integers(1500, 8193))
+        if T * n * D > 40_000_000:
+            continue
+        hc = tuple(float(v) for v in rng.uniform(0.5, 2.0, size=3))
+        out.append(Case(T=T, n=n, D=D, dtype="bf16", hc_scale=hc, repeat=int(rng.choice([3, 20])),
+                        eps=float(rng.choice([1e-6, 1e-3])), pick=int(rng.integers(0, 1 << 20)),
+                        stagger=str(int(rng.integers(0, 2))), seed=int(rng.integers(1, 1 << 30))))
+    return out
+
+
+LONG_CASES = _draw_long(12)
+
+
 def _spec(c):
     fn_std = 0.05 if c.n < 4 else (0.02 if c.n == 4 else 0.03)
     return W.custom(c.T, c.n, c.D, c.dtype, seed=c.seed, fn_std=fn_std, hc_scale=c.hc_scale,
@@ -95,7 +116,7 @@ def _tokens(T, seed):
     return np.unique(np.concatenate([[0, T - 1], np.arange(max(0, T - 40), T), rng.choice(T, 48, replace=False)]))
 
 
-@pytest.mark.parametrize("c", PRE_CASES, ids=str)
+@pytest.mark.parametrize("c", PRE_CASES + LONG_CASES, ids=str)
 def test_pre_sweep(monkeypatch, c):
     monkeypatch.setenv("MHC_STAGGER", c.stagger)
     x = W.generate(_spec(c))
