@@ -54,8 +54,12 @@ int make_pre_plan(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, PrePl
   if (st != MHC_OK) return st;
   if (n_splits < -kMaxSlices || n_splits > 256) return MHC_ERR_INVALID_ARG;
   if (n_splits == 0 && T > 0) {
-    const int t = tuned_splits(T, n, D, dt, boundary);
-    if (t != 0 && make_pre_plan(T, n, D, t, dt, p, boundary) == MHC_OK) return MHC_OK;
+    int stag = -1;
+    const int t = tuned_splits(T, n, D, dt, boundary, &stag);
+    if (t != 0 && make_pre_plan(T, n, D, t, dt, p, boundary) == MHC_OK) {
+      p->rstag = stag;
+      return MHC_OK;
+    }
   }
   PrePlan q{};
   q.T = T;
@@ -117,6 +121,7 @@ int make_pre_plan(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, PrePl
   const bool res_ok = n_splits <= 0 && resident_choose(T, n, D, dt, &rc, boundary, want_S);
   if (n_splits < 0 && !res_ok) return MHC_ERR_UNSUPPORTED;
   q.res = res_ok;
+  q.rstag = -1;
   q.total_bytes = total2;
   if (q.res) {
     q.rS = rc.S;

@@ -29,6 +29,7 @@ struct PrePlan {
   // once (one generation)
   bool res;
   int rS, rcps, rper, rTB;
+  int rstag;             // single-pass instance from the tile table: 0 in step, 1 per wave, -1 the library's rule
   size_t off_fpart, off_pre, off_tags_end;  // tagged exchange words [off_fpart, off_tags_end)
   size_t total_bytes;    // enough for whichever path runs
 };
@@ -49,8 +50,10 @@ constexpr int kStArrive = 24;   // first-use barrier arrivals of the running cal
 constexpr int kSplitsSinglePass = -1;
 constexpr int kMaxSlices = 256;
 
-// The tile table's n_splits for the shape (0 when no entry covers it).
-int tuned_splits(int64_t T, int n, int64_t D, mhc_dtype dt, bool boundary);
+// The tile table's n_splits for the shape (0 when no entry covers it); with
+// `stagger`, also the entry's single-pass kernel instance (0: workgroup in
+// step, 1: one pipeline per wave, -1: the library's rule; -1 when no entry).
+int tuned_splits(int64_t T, int n, int64_t D, mhc_dtype dt, bool boundary, int* stagger = nullptr);
 
 // Fills `p`; returns MHC_OK or the status mhc_pre would return for the sizes.
 // n_splits = 0 takes the tile table's entry when one covers the shape and is

@@ -33,15 +33,17 @@
 //   4. every wave reads pre for its 16 tokens and writes y for its slice.
 // A work item waits only for the items of its tile in the same generation,
 // and every workgroup is resident, so every generation completes.
-// The kernel has two instances. Up to three generations the workgroup keeps
-// its waves in step (barriers between the steps; step 3 finalises TB tokens
-// at a time over the whole workgroup). From four generations on (STAG) every
-// wave runs steps 1-4 on its own 16 rows with no workgroup barrier after the
-// prologue: it finalises the tokens of its rows that fall to slice s and
-// polls only for the pre values of its own rows, so waves drift apart and one
-// wave's exchange waits overlap other waves' loads. The environment variable
-// MHC_STAGGER (0 or 1, read at each launch) forces either instance: a test
-// hook, both give results within the same rounding bounds.
+// The kernel has two instances. In one the workgroup keeps its waves in
+// step (barriers between the steps; step 3 finalises TB tokens at a time
+// over the whole workgroup). In the other (STAG) every wave runs steps 1-4 on
+// its own 16 rows with no workgroup barrier after the prologue: it finalises
+// the tokens of its rows that fall to slice s and polls only for the pre
+// values of its own rows, so waves drift apart and one wave's exchange waits
+// overlap other waves' loads. The tile table picks the instance per shape
+// (measured both ways), and a rule on the number of generations covers the
+// rest. The environment variable MHC_STAGGER (0 or 1, read at each launch)
+// forces either instance: a test hook, both give results within the same
+// rounding bounds.
 //
 // Exchange protocol: every exchanged value is a 64-bit word, tag (low 32 bits
 // of this call's epoch) in the high half and fp32 bits in the low half,
@@ -78,7 +80,15 @@ constexpr int kMaxAVgprsPost = 144;       // residual + block-output registers (
 constexpr int kLdsMax = 160 * 1024;
 constexpr long long kPollTicks = 10000000LL;  // 100 ms of the 100 MHz wall clock
 constexpr int kCpsList[] = {1, 2, 3, 4, 5, 6, 7, 8, 14};
-constexpr int kStaggerGenerations = 4;    // from this many generations on, waves run their own pipelines
+// Without a tile-table entry for the call, waves run their own pipelines
+// from this many generations of resident tiles on (per call after a cache
+// sweep, n = 4: the pre step gains from two generations on, 52.5 -> 51.6 us
+// at T = 2048, D = 7168 and 45.2 -> 42.4 us at D = 5120, but loses at one
+// tile, 14.0 -> 17.6 us at T = 32; the layer boundary loses up to 7 us at
+// four to eight generations at D = 4096 and 5120 and gains only in long runs
+// at D = 7168, 595 -> 579 us at sixteen generations).
+constexpr int kStaggerGenerationsPre = 2;
+constexpr int kStaggerGenerationsBoundary = 12;
 
 typedef unsigned long long u64;
 
@@ -441,15 +451,15 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
     load_cols(tile, std::integral_constant<int, kFirstCols>{}, std::integral_constant<int, CPS>{});
   }
 
-  // STAG (long runs of generations): each wave runs its own pipeline, with
-  // no workgroup barrier, finalising the tokens of its own rows. The waves of
-  // a workgroup drift apart (the first waves of a workgroup get their data
-  // first), so one wave's exchange waits fall into other waves' loads: at
-  // T = 16384, n = 4, D = 7168 (16 generations) a call takes 315 us against
-  // 361 us with the workgroup in step. With two generations (T = 2048) the
-  // exchange polls queue behind the other waves' loads in the CU's memory
-  // pipeline and the call is no faster, so short runs keep the workgroup in
-  // step (it finalises together, TB tokens at a time).
+  // STAG: each wave runs its own pipeline, with no workgroup barrier,
+  // finalising the tokens of its own rows. The waves of a workgroup drift
+  // apart (the first waves of a workgroup get their data first), so one
+  // wave's exchange waits fall into other waves' loads: at T = 16384, n = 4,
+  // D = 7168 (16 generations) pre takes 315 us against 361 us with the
+  // workgroup in step. A single tile is faster in step (its fn-first
+  // prologue leaves HBM idle while fn is packed), and so is the layer
+  // boundary at up to eight generations (measured at D = 4096, 5120 and
+  // 7168). In step, the workgroup finalises together, TB tokens at a time.
   auto generation = [&](auto next_tag) {
     constexpr bool NEXT = decltype(next_tag)::value;
     // this tile's residual slice is in flight (rows past T read the tile's
@@ -1061,8 +1071,16 @@ long long poll_ticks() {
   return kPollTicks;
 }
 
+// The single-pass instance by rule (the tile table's entry decides when one
+// covers the call).
+bool stagger_by_rule(int64_t tiles, int per, bool boundary) {
+  const int64_t gens = (tiles + per - 1) / per;
+  return gens >= (boundary ? kStaggerGenerationsBoundary : kStaggerGenerationsPre);
+}
+
 ResArgs resident_args(const PrePlan& p, const void* residual, const float* fn, const float* hc_scale,
-                      const float* bias, float* post, float* comb, void* y, void* workspace, int repeat, float eps) {
+                      const float* bias, float* post, float* comb, void* y, void* workspace, int repeat, float eps,
+                      bool boundary) {
   char* ws = static_cast<char*>(workspace);
   ResArgs a{};
   a.x = static_cast<const uint16_t*>(residual);
@@ -1089,7 +1107,7 @@ ResArgs resident_args(const PrePlan& p, const void* residual, const float* fn, c
   a.K = (float)p.K;
   a.poll_ticks = poll_ticks();
   const int64_t tiles = (p.T + kTM - 1) / kTM;
-  a.stagger = tiles >= (int64_t)kStaggerGenerations * p.rper ? 1 : 0;
+  a.stagger = p.rstag >= 0 ? p.rstag : (stagger_by_rule(tiles, p.rper, boundary) ? 1 : 0);
   // test hook: MHC_STAGGER = 1 or 0 forces the instance at any size
   if (const char* e = std::getenv("MHC_STAGGER")) a.stagger = *e == '1' ? 1 : (*e == '0' ? 0 : a.stagger);
   return a;
@@ -1099,7 +1117,7 @@ ResArgs resident_args(const PrePlan& p, const void* residual, const float* fn, c
 hipError_t launch_pre_resident(const PrePlan& p, const void* residual, const float* fn, const float* hc_scale,
                                const float* bias, float* post, float* comb, void* y, void* workspace, int repeat,
                                float eps, hipStream_t s) {
-  const ResArgs a = resident_args(p, residual, fn, hc_scale, bias, post, comb, y, workspace, repeat, eps);
+  const ResArgs a = resident_args(p, residual, fn, hc_scale, bias, post, comb, y, workspace, repeat, eps, false);
   dispatch(p.n, p.rcps, Launcher<false>{&a, (unsigned)a.P, s});
   return hipGetLastError();
 }
@@ -1108,7 +1126,7 @@ hipError_t launch_post_pre_resident(const PrePlan& p, const void* h, const void*
                                     const float* comb_in, void* out, const float* fn, const float* hc_scale,
                                     const float* bias, float* post, float* comb, void* y, void* workspace,
                                     int repeat, float eps, hipStream_t s) {
-  ResArgs a = resident_args(p, residual, fn, hc_scale, bias, post, comb, y, workspace, repeat, eps);
+  ResArgs a = resident_args(p, residual, fn, hc_scale, bias, post, comb, y, workspace, repeat, eps, true);
   a.h = static_cast<const uint16_t*>(h);
   a.post_in = post_in;
   a.comb_in = comb_in;

@@ -5,7 +5,9 @@ The split-K pre GEMM is tiled over the hidden axis with a block size picked per
 hidden size ([P1] "[sglang] AMD ROCm DeepSeek-V4 performance optimisation:
 Aiter MHC kernel integration analysis", section 3, TileLang kernel tuning).
 Here the choices are the single-pass kernel's slice count S (n_splits = -S,
-D = 32 * cps * S) and the two-pass path's split count (n_splits = S > 0). For
+D = 32 * cps * S) together with its instance (the workgroup's waves in step,
+or one pipeline per wave; chosen through MHC_STAGGER while timing), and the
+two-pass path's split count (n_splits = S > 0). For
 every (op, n, D, dtype) and every token count T of a sweep, each candidate is
 timed over back-to-back calls that rotate over input sets (enough of them
 that the other sets move twice the 256 MB Infinity Cache between two uses of
@@ -45,8 +47,9 @@ KEEP_LIBRARY_WITHIN = 1.03
 T_MAX = 2 ** 31 - 1
 
 
-def candidates(op: str, T: int, n: int, D: int, dt: int) -> list[int]:
-    """n_splits values the library accepts for the shape: single-pass slice counts, then two-pass splits."""
+def candidates(op: str, T: int, n: int, D: int, dt: int) -> list[tuple[int, int]]:
+    """(n_splits, instance) pairs the library accepts for the shape: each single-pass slice count with the
+    waves in step (0) and with one pipeline per wave (1), then the two-pass split counts (instance -1)."""
     L = mhc.lib()
     out = []
     for S in range(2, 257):
@@ -54,11 +57,24 @@ def candidates(op: str, T: int, n: int, D: int, dt: int) -> list[int]:
             continue
         if op == "boundary" and L.mhc_post_pre_fused(T, n, D, -S, dt) != 1:
             continue
-        out.append(-S)
+        out += [(-S, 0), (-S, 1)]
     for S in TWO_PASS_SPLITS:
         if L.mhc_pre_splits(T, n, D, S, dt) == S:
-            out.append(S)
+            out.append((S, -1))
     return out
+
+
+def key(c: tuple[int, int]) -> str:
+    """Record key of a candidate: '-32/1' (single-pass, instance) or '8' (two-pass)."""
+    return f"{c[0]}/{c[1]}" if c[0] < 0 else str(c[0])
+
+
+def _instance(c: tuple[int, int]) -> None:
+    import os
+    if c[1] < 0:
+        os.environ.pop("MHC_STAGGER", None)
+    else:
+        os.environ["MHC_STAGGER"] = str(c[1])
 
 
 def set_count(T: int, n: int, D: int, elem: int) -> int:
@@ -119,36 +135,37 @@ def time_candidate(torch, op: str, inputs: _Inputs, n_splits: int, ws, iters: in
     return e0.elapsed_time(e1) * 1000.0 / iters
 
 
-def pick(times: dict[int, float], library: int | None) -> int:
+def pick(times: dict, library=None):
     best = min(times, key=times.get)
     if library is not None and library in times and times[library] <= times[best] * KEEP_LIBRARY_WITHIN:
         return library
     return best
 
 
-def ranges(points: list[tuple[int, int]]) -> list[tuple[int, int, int]]:
-    """[(T, n_splits)] sorted by T -> [(T_lo, T_hi, n_splits)], neighbours with one choice merged."""
+def ranges(points: list[tuple]) -> list[tuple]:
+    """[(T, choice...)] sorted by T -> [(T_lo, T_hi, choice...)], neighbours with one choice merged."""
     out = []
-    for i, (T, ns) in enumerate(points):
+    for i, (T, *choice) in enumerate(points):
         lo = 1 if i == 0 else int(math.sqrt(points[i - 1][0] * T)) + 1
         hi = T_MAX if i == len(points) - 1 else int(math.sqrt(T * points[i + 1][0]))
-        if out and out[-1][2] == ns:
-            out[-1] = (out[-1][0], hi, ns)
+        if out and list(out[-1][2:]) == choice:
+            out[-1] = (out[-1][0], hi, *choice)
         else:
-            out.append((lo, hi, ns))
+            out.append((lo, hi, *choice))
     return out
 
 
 def write_cpp(path: str, entries: list[dict], device: str, stamp: str) -> None:
     lines = []
     for e in entries:
-        for lo, hi, ns in ranges([(p["T"], p["best"]) for p in e["points"]]):
-            lines.append(f"    {{{0 if e['op'] == 'pre' else 1}, {e['n']}, {e['D']}, {e['dt']}, {lo}, {hi}, {ns}}},")
+        for lo, hi, ns, st in ranges([(p["T"], p["best"], p["stagger"]) for p in e["points"]]):
+            lines.append(f"    {{{0 if e['op'] == 'pre' else 1}, {e['n']}, {e['D']}, {e['dt']}, {lo}, {hi}, {ns}, {st}}},")
     body = "\n".join(lines)
-    text = f"""// Tile table: the n_splits that measured fastest for listed shapes (op, n, D,
-// dtype, token range). Written by mhc_hyper_connection_pre_amd/tune.py; the
-// library's choice (n_splits = 0) takes an entry that covers the call and is
-// valid for it, and its heuristic otherwise.
+    text = f"""// Tile table: the n_splits (and for the single-pass kernel its instance) that
+// measured fastest for listed shapes (op, n, D, dtype, token range). Written
+// by mhc_hyper_connection_pre_amd/tune.py; the library's choice (n_splits = 0)
+// takes an entry that covers the call and is valid for it, and its heuristic
+// otherwise.
 // Measured on {device} ({stamp}).
 
 #include "mhc_internal.h"
@@ -163,19 +180,23 @@ struct TileEntry {{
   int dt;               // mhc_dtype
   int64_t T_lo, T_hi;   // token counts the entry covers, inclusive
   int n_splits;         // -S: single-pass with S slices; S > 0: two-pass with S splits
+  int stagger;          // single-pass instance: 0 waves in step, 1 one pipeline per wave; -1 the library's rule
 }};
 
 constexpr TileEntry kTable[] = {{
 {body}
-    {{-1, 0, 0, 0, 0, 0, 0}},   // end
+    {{-1, 0, 0, 0, 0, 0, 0, -1}},   // end
 }};
 
 }}  // namespace
 
-int tuned_splits(int64_t T, int n, int64_t D, mhc_dtype dt, bool boundary) {{
+int tuned_splits(int64_t T, int n, int64_t D, mhc_dtype dt, bool boundary, int* stagger) {{
+  if (stagger) *stagger = -1;
   for (const TileEntry& e : kTable) {{
-    if (e.op == (boundary ? 1 : 0) && e.n == n && e.D == D && e.dt == (int)dt && T >= e.T_lo && T <= e.T_hi)
+    if (e.op == (boundary ? 1 : 0) && e.n == n && e.D == D && e.dt == (int)dt && T >= e.T_lo && T <= e.T_hi) {{
+      if (stagger) *stagger = e.stagger;
       return e.n_splits;
+    }}
   }}
   return 0;
 }}
@@ -220,22 +241,27 @@ def main(argv=None) -> int:
                 if not cands:
                     continue
                 inputs = _Inputs(torch, T, n, D, dtype, seed=T * 31 + D)
-                need = max(L.mhc_pre_workspace_bytes(T, n, D, c, dt) for c in cands)
+                need = max(L.mhc_pre_workspace_bytes(T, n, D, c[0], dt) for c in cands)
                 ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
                 ws[:256].zero_()
                 runs = {c: [] for c in cands}
                 for _ in range(args.rounds):
                     for c in cands:
-                        runs[c].append(time_candidate(torch, op, inputs, c, ws, args.iters, args.warmup))
+                        _instance(c)
+                        runs[c].append(time_candidate(torch, op, inputs, c[0], ws, args.iters, args.warmup))
+                _instance((0, -1))
                 times = {c: statistics.median(v) for c, v in runs.items()}
                 lib_sp = L.mhc_pre_splits(T, n, D, -1, dt)
-                library = -lib_sp if lib_sp > 0 and -lib_sp in times else None
+                # the library's own single-pass slicing, in the faster of its two instances
+                lib = [c for c in times if c[0] == -lib_sp] if lib_sp > 0 else []
+                library = min(lib, key=times.get) if lib else None
                 best = pick(times, library)
-                e["points"].append({"T": T, "best": best, "library_single_pass": library,
-                                    "us": {str(c): round(v, 2) for c, v in times.items()}})
-                print(f"{op:8s} n={n} D={D} {dname} T={T:6d}: best n_splits {best:4d} "
+                e["points"].append({"T": T, "best": best[0], "stagger": best[1],
+                                    "library_single_pass": None if library is None else key(library),
+                                    "us": {key(c): round(v, 2) for c, v in times.items()}})
+                print(f"{op:8s} n={n} D={D} {dname} T={T:6d}: best {key(best):>8s} "
                       f"({times[best]:.1f} us; library single-pass "
-                      f"{'-' if library is None else f'{library} {times[library]:.1f} us'})", flush=True)
+                      f"{'-' if library is None else f'{key(library)} {times[library]:.1f} us'})", flush=True)
                 del inputs, ws
                 torch.cuda.empty_cache()
             entries.append(e)

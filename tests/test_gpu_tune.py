@@ -74,7 +74,10 @@ def test_tuner_short_run(tmp_path):
     for e in d["entries"]:
         assert [p["T"] for p in e["points"]] == [64, 300]
         for p in e["points"]:
-            times = {int(k): v for k, v in p["us"].items()}
-            assert p["best"] in times and all(v > 0 for v in times.values())
-            assert set(times) == set(tune.candidates(e["op"], p["T"], 4, 1024, 0))
+            times = p["us"]
+            best = (p["best"], p["stagger"])
+            assert tune.key(best) in times and all(v > 0 for v in times.values())
+            assert set(times) == {tune.key(c) for c in tune.candidates(e["op"], p["T"], 4, 1024, 0)}
+            # each single-pass slicing is timed in both kernel instances
+            assert {k.split("/")[1] for k in times if "/" in k} == {"0", "1"}
     assert "kTable" in cpp.read_text()

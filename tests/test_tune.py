@@ -18,6 +18,9 @@ def test_ranges_merge_and_cover():
     # the boundary between 64 and 256 sits at their geometric mean
     assert r[0][1] == 128 and r[1][0] == 129
     assert tune.ranges([(2048, -32)]) == [(1, tune.T_MAX, -32)]
+    # with the kernel instance: a change of instance alone starts a new range
+    r2 = tune.ranges([(64, -80, 0), (256, -80, 0), (2048, -80, 1), (16384, -32, 1)])
+    assert [c for _, _, *c in r2] == [[-80, 0], [-80, 1], [-32, 1]]
 
 
 def test_pick_keeps_library_tiling_within_three_percent():
@@ -28,15 +31,18 @@ def test_pick_keeps_library_tiling_within_three_percent():
 
 def test_generated_table_compiles(tmp_path):
     entries = [{"op": "pre", "n": 4, "D": 7168, "dtype": "bf16", "dt": 0,
-                "points": [{"T": 64, "best": -56}, {"T": 2048, "best": -32}]},
+                "points": [{"T": 64, "best": -56, "stagger": 0}, {"T": 2048, "best": -32, "stagger": 1}]},
                {"op": "boundary", "n": 4, "D": 5120, "dtype": "bf16", "dt": 0,
-                "points": [{"T": 32, "best": -80}]}]
+                "points": [{"T": 32, "best": -80, "stagger": 0}]},
+               {"op": "pre", "n": 8, "D": 4096, "dtype": "bf16", "dt": 0,
+                "points": [{"T": 32, "best": 16, "stagger": -1}]}]
     src = tmp_path / "table.cpp"
     tune.write_cpp(str(src), entries, "test device", "now")
     text = src.read_text()
-    assert "{0, 4, 7168, 0, 1, 362, -56}," in text
-    assert "{0, 4, 7168, 0, 363, 2147483647, -32}," in text
-    assert "{1, 4, 5120, 0, 1, 2147483647, -80}," in text
+    assert "{0, 4, 7168, 0, 1, 362, -56, 0}," in text
+    assert "{0, 4, 7168, 0, 363, 2147483647, -32, 1}," in text
+    assert "{1, 4, 5120, 0, 1, 2147483647, -80, 0}," in text
+    assert "{0, 8, 4096, 0, 1, 2147483647, 16, -1}," in text
     cc = build.hipcc()
     inc = os.path.join(build.PKG, "csrc")
     r = subprocess.run([cc, *build.COMMON_FLAGS, f"-I{inc}", "-c", str(src), "-o", str(tmp_path / "t.o")],
@@ -60,9 +66,10 @@ def test_committed_table_matches_its_record():
     import mhc_hyper_connection_pre_amd as mhc
     L = mhc.lib()
     for e in d["entries"]:
-        for lo, hi, ns in tune.ranges([(p["T"], p["best"]) for p in e["points"]]):
+        for lo, hi, ns, st in tune.ranges([(p["T"], p["best"], p["stagger"]) for p in e["points"]]):
             op = 0 if e["op"] == "pre" else 1
-            assert f"{{{op}, {e['n']}, {e['D']}, {e['dt']}, {lo}, {hi}, {ns}}}," in text
+            assert f"{{{op}, {e['n']}, {e['D']}, {e['dt']}, {lo}, {hi}, {ns}, {st}}}," in text
+            assert ns < 0 or st == -1   # an instance only for the single-pass kernel
         # the library's choice at every measured token count is the measured best
         for p in e["points"]:
             want = p["best"]
