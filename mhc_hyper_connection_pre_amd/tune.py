@@ -35,6 +35,7 @@ import argparse
 import datetime
 import json
 import math
+import os
 import statistics
 import sys
 
@@ -69,12 +70,18 @@ def key(c: tuple[int, int]) -> str:
     return f"{c[0]}/{c[1]}" if c[0] < 0 else str(c[0])
 
 
+_CALLER_STAGGER = os.environ.get("MHC_STAGGER")
+
+
 def _instance(c: tuple[int, int]) -> None:
-    import os
-    if c[1] < 0:
+    """Select the single-pass instance for the next calls (MHC_STAGGER is read at each launch); instance -1
+    restores the caller's setting."""
+    if c[1] >= 0:
+        os.environ["MHC_STAGGER"] = str(c[1])
+    elif _CALLER_STAGGER is None:
         os.environ.pop("MHC_STAGGER", None)
     else:
-        os.environ["MHC_STAGGER"] = str(c[1])
+        os.environ["MHC_STAGGER"] = _CALLER_STAGGER
 
 
 def set_count(T: int, n: int, D: int, elem: int) -> int:
