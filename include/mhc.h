@@ -120,10 +120,11 @@ MHC_API size_t mhc_pre_workspace_bytes(int64_t T, int n, int64_t D, int n_splits
  *   slice tiling fits (mhc_pre_splits(..., -1, ...) > 0) and a 16-byte
  *   aligned fn; n_splits = 0 takes it when it can. Otherwise the two-pass
  *   path runs (pack fn, split-K GEMM, then an epilogue that reads the
- *   residual again for y). The single-pass kernel keeps each workgroup's
- *   waves in step up to three generations of resident tiles and runs one
- *   pipeline per wave from four on; the environment variable MHC_STAGGER
- *   (0 or 1, read at each launch) forces either, as a test hook.
+ *   residual again for y). The single-pass kernel either keeps each
+ *   workgroup's waves in step or runs one pipeline per wave; the tile table
+ *   picks per shape (measured), else a rule on the number of generations of
+ *   resident tiles; the environment variable MHC_STAGGER (0 or 1, read at
+ *   each launch) forces either, as a test hook.
  * Co-residency: the single-pass kernel's workgroups wait for one another, so
  *   the launch is sized to what the device holds at once (workgroups per CU
  *   from the occupancy query times the CUs). Work that holds CUs while it
