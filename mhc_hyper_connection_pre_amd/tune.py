@@ -9,11 +9,12 @@ D = 32 * cps * S) together with its instance (the workgroup's waves in step,
 or one pipeline per wave; chosen through MHC_STAGGER while timing), and the
 two-pass path's split count (n_splits = S > 0). For
 every (op, n, D, dtype) and every token count T of a sweep, each candidate is
-timed over back-to-back calls that rotate over input sets (enough of them
-that the other sets move twice the 256 MB Infinity Cache between two uses of
-one, so it does not serve a repeated input), between two HIP events on the
-launch stream, in several rounds that visit the candidates in turn; a
-candidate's time is its median over the rounds. The fastest becomes the table
+timed call by call, each call after a read of a 1 GiB buffer (so neither L2
+nor the 256 MB Infinity Cache holds its inputs, as between a layer's calls in
+a model and as bench.py times them), between two HIP events on the launch
+stream, over input sets it rotates through, in several rounds that visit the
+candidates in turn; a candidate's time is its median over the rounds
+(--back-to-back times back-to-back calls instead). The fastest becomes the table
 entry for the token range around T (range ends at the geometric means of
 neighbouring sweep points); the library's own single-pass tiling is kept when
 it is within 3 % of the fastest, so noise does not flip the choice.
@@ -126,20 +127,34 @@ def _call(op: str, s: dict, n_splits: int, ws) -> None:
                          workspace=ws)
 
 
-def time_candidate(torch, op: str, inputs: _Inputs, n_splits: int, ws, iters: int, warmup: int) -> float:
-    """Microseconds per call: `iters` back-to-back calls between two events, after `warmup` calls."""
+def time_candidate(torch, op: str, inputs: _Inputs, n_splits: int, ws, iters: int, warmup: int,
+                   sweep=None) -> float:
+    """Microseconds per call, after `warmup` calls. Without `sweep`: `iters` back-to-back calls between two
+    events. With `sweep` (a device buffer of 1 GiB): each call alone between two events after a read of the
+    whole buffer, which leaves neither L2 nor the memory-side cache holding its inputs (as between a layer's
+    calls in a model, and as bench.py times them); the median of `iters` calls."""
     k = len(inputs.sets)
     for i in range(warmup):
         _call(op, inputs.sets[i % k], n_splits, ws)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
+    if sweep is None:
+        e0.record()
+        for i in range(iters):
+            _call(op, inputs.sets[i % k], n_splits, ws)
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / iters
+    ts = []
     for i in range(iters):
+        sweep.max()
+        e0.record()
         _call(op, inputs.sets[i % k], n_splits, ws)
-    e1.record()
-    e1.synchronize()
-    return e0.elapsed_time(e1) * 1000.0 / iters
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1000.0)
+    return statistics.median(ts)
 
 
 def pick(times: dict, library=None):
@@ -222,6 +237,8 @@ def main(argv=None) -> int:
     ap.add_argument("--iters", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--rounds", type=int, default=3)
+    ap.add_argument("--back-to-back", action="store_true",
+                    help="time back-to-back calls instead of each call after a 1 GiB read sweep")
     ap.add_argument("--json", default=None, help="write every measurement here")
     ap.add_argument("--cpp", default=None, help="write the library's tile table source here")
     args = ap.parse_args(argv)
@@ -234,6 +251,7 @@ def main(argv=None) -> int:
     device = f"{props.name} ({props.gcnArchName.split(':')[0]}, {props.multi_processor_count} CUs)"
     stamp = datetime.datetime.now(datetime.timezone.utc).strftime("%Y-%m-%d %H:%M UTC")
     L = mhc.lib()
+    sweep = None if args.back_to_back else torch.ones(1 << 28, dtype=torch.int32, device="cuda")
     entries = []
     for shape in args.shapes:
         parts = shape.split(",")
@@ -255,7 +273,7 @@ def main(argv=None) -> int:
                 for _ in range(args.rounds):
                     for c in cands:
                         _instance(c)
-                        runs[c].append(time_candidate(torch, op, inputs, c[0], ws, args.iters, args.warmup))
+                        runs[c].append(time_candidate(torch, op, inputs, c[0], ws, args.iters, args.warmup, sweep))
                 _instance((0, -1))
                 times = {c: statistics.median(v) for c, v in runs.items()}
                 lib_sp = L.mhc_pre_splits(T, n, D, -1, dt)
@@ -275,7 +293,8 @@ def main(argv=None) -> int:
     if args.json:
         with open(args.json, "w") as f:
             json.dump({"device": device, "measured": stamp, "iters": args.iters, "warmup": args.warmup,
-                       "rounds": args.rounds, "entries": entries}, f, indent=1)
+                       "rounds": args.rounds, "timing": "back to back" if args.back_to_back else
+                       "each call after a 1 GiB read sweep", "entries": entries}, f, indent=1)
     if args.cpp:
         write_cpp(args.cpp, entries, device, stamp)
     return 0
