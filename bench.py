@@ -61,9 +61,9 @@ CSRC = os.path.join(ROOT, "mhc_hyper_connection_pre_amd", "csrc")
 # workload: the profile file and the sources its number holds for.
 _RESIDENT_SOURCES = ["mhc_pre_resident.hip", "mhc_device.h", "mhc_pack.h", "mhc_epilogue.h", "mhc_internal.h"]
 TRAFFIC = {
-    "pre": ("traffic_pre_resident_prefill-d7168.txt", "pre_resident_kernel<4, 7, false, false>", _RESIDENT_SOURCES),
+    "pre": ("traffic_pre_resident_prefill-d7168.txt", "pre_resident_kernel<4, 7, false,", _RESIDENT_SOURCES),
     "post": ("traffic_post_prefill-d7168.txt", "post_kernel<", ["mhc_post.hip", "mhc_device.h"]),
-    "boundary": ("traffic_boundary_prefill-d7168.txt", "pre_resident_kernel<4, 7, true, false>", _RESIDENT_SOURCES),
+    "boundary": ("traffic_boundary_prefill-d7168.txt", "pre_resident_kernel<4, 7, true,", _RESIDENT_SOURCES),
 }
 COPY_KIB = 1 << 20   # the 1 GiB calibration copy bench.py runs, in KiB read and written
 
