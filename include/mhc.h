@@ -241,6 +241,21 @@ MHC_API int mhc_post_pre(void* out, float* post_next, float* comb_next, void* y_
 MHC_API int mhc_post_pre_fused(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt);
 
 /*
+ * The plan of an mhc_pre (boundary = 0) or mhc_post_pre (boundary = 1) call
+ * with these sizes on the current device (given a 16-byte aligned fn), for
+ * tests and tuning ([P1] section 3: the hidden-axis tiling is chosen per
+ * shape). info must hold 5 ints: info[0] = 1 for the single-pass kernel, 0 for
+ * the two-pass path; info[1] = its slices of the hidden axis, or the two-pass
+ * split count; info[2] = 32-wide columns per slice (single-pass, else 0);
+ * info[3] = generations of resident token tiles (single-pass, else 0);
+ * info[4] = the single-pass kernel's instance, 1 for one pipeline per wave,
+ * 0 for the workgroup's waves in step (-1 for the two-pass path). Returns
+ * MHC_OK, MHC_ERR_INVALID_ARG for a NULL info, or the status the call would
+ * return for the sizes; info is written only on MHC_OK.
+ */
+MHC_API int mhc_pre_plan_info(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, int boundary, int* info);
+
+/*
  * mhc_post_combine_norm - [P2] section 1 (post mix, combine into one bf16
  * row, RMSNorm, one row per workgroup) and section 2 (the row is stored as
  * `normalized`):

@@ -23,7 +23,7 @@ import os
 __all__ = [
     "MhcError", "lib", "library_path", "mhc_pre", "mhc_post", "mhc_post_combine_norm",
     "mhc_pre_workspace_bytes", "mhc_pre_splits", "mhc_pre_sync_timeouts", "mhc_post_pre", "mhc_post_pre_fused",
-    "mhc_pre_static", "MHC_PRE_STATIC_SCRATCH_BYTES", "MHC_BF16", "MHC_F32", "PreparedCall",
+    "mhc_pre_static", "mhc_pre_plan_info", "MHC_PRE_STATIC_SCRATCH_BYTES", "MHC_BF16", "MHC_F32", "PreparedCall",
 ]
 
 MHC_BF16 = 0
@@ -88,6 +88,8 @@ def load_library(path: str) -> ctypes.CDLL:
     L.mhc_post_pre.restype = I
     L.mhc_post_pre_fused.argtypes = [I64, I, I64, I, I]
     L.mhc_post_pre_fused.restype = I
+    L.mhc_pre_plan_info.argtypes = [I64, I, I64, I, I, I, ctypes.POINTER(I)]
+    L.mhc_pre_plan_info.restype = I
     return L
 
 
@@ -190,6 +192,17 @@ def mhc_pre_splits(T: int, n: int, D: int, n_splits: int = 0, dtype_code: int = 
     if st < 0:
         raise MhcError("mhc_pre_splits", st)
     return st
+
+
+def mhc_pre_plan_info(T: int, n: int, D: int, n_splits: int = 0, dtype_code: int = MHC_BF16,
+                      boundary: bool = False) -> dict:
+    """The plan a call with these sizes takes (``include/mhc.h``: mhc_pre_plan_info)."""
+    info = (ctypes.c_int * 5)()
+    st = lib().mhc_pre_plan_info(T, n, D, n_splits, dtype_code, 1 if boundary else 0, info)
+    if st != 0:
+        raise MhcError("mhc_pre_plan_info", st)
+    return {"single_pass": bool(info[0]), "splits": info[1], "cols_per_slice": info[2], "generations": info[3],
+            "per_wave": info[4] == 1 if info[0] else None}
 
 
 def mhc_pre_workspace_bytes(T: int, n: int, D: int, n_splits: int = 0, dtype_code: int = MHC_BF16) -> int:

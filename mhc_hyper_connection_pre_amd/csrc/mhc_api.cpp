@@ -269,6 +269,28 @@ MHC_API int mhc_post_pre_fused(int64_t T, int n, int64_t D, int n_splits, mhc_dt
   return st != MHC_OK ? st : (p.res ? 1 : 0);
 }
 
+MHC_API int mhc_pre_plan_info(int64_t T, int n, int64_t D, int n_splits, mhc_dtype dt, int boundary, int* info) {
+  if (info == nullptr) return MHC_ERR_INVALID_ARG;
+  PrePlan p;
+  const int st = make_pre_plan(T, n, D, n_splits, dt, &p, boundary != 0);
+  if (st != MHC_OK) return st;
+  if (p.res) {
+    const int64_t tiles = (T + kResidentTile - 1) / kResidentTile;
+    info[0] = 1;
+    info[1] = p.rS;
+    info[2] = p.rcps;
+    info[3] = (int)(p.rper > 0 ? (tiles + p.rper - 1) / p.rper : 0);
+    info[4] = resident_stagger(p, boundary != 0);
+  } else {
+    info[0] = 0;
+    info[1] = p.S;
+    info[2] = 0;
+    info[3] = 0;
+    info[4] = -1;
+  }
+  return MHC_OK;
+}
+
 MHC_API int mhc_pre(float* post, float* comb, void* y, const void* residual, mhc_dtype dt, const float* fn,
                     const float* hc_scale, const float* bias, int64_t T, int n, int64_t D, int sinkhorn_repeat,
                     float eps, int n_splits, void* workspace, size_t workspace_bytes, void* stream) {

@@ -78,6 +78,10 @@ hipError_t launch_post_pre_resident(const PrePlan& p, const void* h, const void*
                                     const float* comb_in, void* out, const float* fn, const float* hc_scale,
                                     const float* bias, float* post, float* comb, void* y, void* workspace,
                                     int repeat, float eps, hipStream_t s);
+// The single-pass kernel instance a call with plan `p` runs: 1 one pipeline
+// per wave, 0 the workgroup's waves in step (the tile table's choice, else
+// a rule on the number of generations; MHC_STAGGER = 0 / 1 overrides).
+int resident_stagger(const PrePlan& p, bool boundary);
 // Single-pass tiling for the shape on the current device (or a 256-CU MI355X
 // when no device is visible): false if the shape is not supported. want_S > 0
 // restricts the choice to that many slices of the hidden axis.

@@ -1071,12 +1071,6 @@ long long poll_ticks() {
   return kPollTicks;
 }
 
-// The single-pass instance by rule (the tile table's entry decides when one
-// covers the call).
-bool stagger_by_rule(int64_t tiles, int per, bool boundary) {
-  const int64_t gens = (tiles + per - 1) / per;
-  return gens >= (boundary ? kStaggerGenerationsBoundary : kStaggerGenerationsPre);
-}
 
 ResArgs resident_args(const PrePlan& p, const void* residual, const float* fn, const float* hc_scale,
                       const float* bias, float* post, float* comb, void* y, void* workspace, int repeat, float eps,
@@ -1106,13 +1100,20 @@ ResArgs resident_args(const PrePlan& p, const void* residual, const float* fn, c
   a.eps = eps;
   a.K = (float)p.K;
   a.poll_ticks = poll_ticks();
-  const int64_t tiles = (p.T + kTM - 1) / kTM;
-  a.stagger = p.rstag >= 0 ? p.rstag : (stagger_by_rule(tiles, p.rper, boundary) ? 1 : 0);
-  // test hook: MHC_STAGGER = 1 or 0 forces the instance at any size
-  if (const char* e = std::getenv("MHC_STAGGER")) a.stagger = *e == '1' ? 1 : (*e == '0' ? 0 : a.stagger);
+  a.stagger = resident_stagger(p, boundary);
   return a;
 }
 }  // namespace
+
+int resident_stagger(const PrePlan& p, bool boundary) {
+  const int64_t tiles = (p.T + kTM - 1) / kTM;
+  const int64_t gens = p.rper > 0 ? (tiles + p.rper - 1) / p.rper : 1;
+  int st = p.rstag >= 0 ? p.rstag
+                        : (gens >= (boundary ? kStaggerGenerationsBoundary : kStaggerGenerationsPre) ? 1 : 0);
+  // test hook: MHC_STAGGER = 1 or 0 forces the instance at any size
+  if (const char* e = std::getenv("MHC_STAGGER")) st = *e == '1' ? 1 : (*e == '0' ? 0 : st);
+  return st;
+}
 
 hipError_t launch_pre_resident(const PrePlan& p, const void* residual, const float* fn, const float* hc_scale,
                                const float* bias, float* post, float* comb, void* y, void* workspace, int repeat,

@@ -294,3 +294,42 @@ def test_binding_raises_without_gpu_tensors(L):
         mhc.mhc_post_combine_norm(h, x, p, c, torch.zeros(2, 4), torch.ones(8))
     with pytest.raises(ValueError, match="GPU"):
         mhc.mhc_pre_sync_timeouts(torch.zeros(256, dtype=torch.uint8), x)
+
+
+def test_pre_plan_info(L, monkeypatch):
+    import json
+    info = (ctypes.c_int * 5)()
+    assert L.mhc_pre_plan_info(2048, 4, 7168, 0, BF16, 0, None) == INVALID
+    assert L.mhc_pre_plan_info(1, 5, 8, 0, BF16, 0, info) == UNSUPPORTED
+    assert L.mhc_pre_plan_info(2048, 4, 7168, -257, BF16, 0, info) == INVALID
+    monkeypatch.delenv("MHC_STAGGER", raising=False)
+    # every measured point of the tile table: the plan takes the entry's tiling and instance
+    table = json.load(open(os.path.join(ROOT, "mhc_hyper_connection_pre_amd", "tile_table.json")))
+    for e in table["entries"]:
+        for p in e["points"]:
+            args = (p["T"], e["n"], e["D"], 0, e["dt"], 1 if e["op"] == "boundary" else 0)
+            assert L.mhc_pre_plan_info(*args, info) == OK, args
+            got = list(info)
+            if p["best"] < 0:
+                S = -p["best"]
+                assert got[:2] == [1, S] and got[2] * 32 * S == e["D"], (args, got)
+                assert got[3] >= 1, (args, got)
+                assert got[4] == p["stagger"], (args, got, p)
+            else:
+                assert got == [0, p["best"], 0, 0, -1], (args, got)
+            if e["op"] == "pre":
+                assert L.mhc_pre_splits(*args[:5]) == abs(p["best"]), args
+    # explicit knobs: a single-pass slice count and a two-pass split count
+    assert L.mhc_pre_plan_info(2048, 4, 7168, -56, BF16, 0, info) == OK and list(info)[:3] == [1, 56, 4]
+    assert L.mhc_pre_plan_info(2048, 4, 7168, 8, BF16, 0, info) == OK and list(info) == [0, 8, 0, 0, -1]
+    assert L.mhc_pre_plan_info(64, 4, 256, 0, F32, 0, info) == OK and info[0] == 0 and info[4] == -1
+    # the instance follows MHC_STAGGER when it is set, for either step
+    for boundary in (0, 1):
+        for v in ("0", "1"):
+            monkeypatch.setenv("MHC_STAGGER", v)
+            assert L.mhc_pre_plan_info(2048, 4, 7168, -32, BF16, boundary, info) == OK
+            assert list(info)[:3] == [1, 32, 7] and info[4] == int(v)
+    # without the table (an explicit slice count): the rule, by generations of resident tiles
+    monkeypatch.delenv("MHC_STAGGER")
+    assert L.mhc_pre_plan_info(128, 4, 7168, -32, BF16, 0, info) == OK and info[3] == 1 and info[4] == 0
+    assert L.mhc_pre_plan_info(16384, 4, 7168, -32, BF16, 1, info) == OK and info[3] >= 12 and info[4] == 1
