@@ -145,6 +145,17 @@ def counter_values(d, counter):
     return out
 
 
+# the counter passes behind the traffic profiles (recorded in each profile unless --traffic-command is given)
+TRAFFIC_COMMAND = [
+    "export TMPDIR=/tmp; R=$PWD; cd /tmp",
+    "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc_fetch -o f --output-format csv -- "
+    "python3 $R/bench.py --steps 4 --warmup 2 --no-cpu-baseline",
+    "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/pmc_write -o w --output-format csv -- "
+    "python3 $R/bench.py --steps 4 --warmup 2 --no-cpu-baseline",
+    "cd $R; python3 bench.py --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write",
+]
+
+
 def write_traffic(fetch_dir, write_dir, command):
     """Write the traffic profiles of the pre and post kernels from a FETCH_SIZE and a WRITE_SIZE pass over
     the default bench run. Each counter is scaled by what it reads for the 1 GiB copy the same run makes
@@ -167,7 +178,7 @@ def write_traffic(fetch_dir, write_dir, command):
         with open(os.path.join(PROFILES, fname), "w") as f:
             f.write(f"# HBM traffic of {k}, prefill T=2048 n=4 D=7168 bf16, per launch\n")
             f.write("# two rocprofv3 counter passes (one counter each), from the repository root on an MI355X:\n")
-            for line in command:
+            for line in command or TRAFFIC_COMMAND:
                 f.write(f"#   {line}\n")
             f.write(f"# calibration: the 1 GiB copy reads FETCH_SIZE {max(fetch[copy[0]]):.0f} KiB and WRITE_SIZE "
                     f"{max(write[copy[0]]):.0f} KiB per dispatch: scales {fs:.5f} and {ws:.5f}\n")
