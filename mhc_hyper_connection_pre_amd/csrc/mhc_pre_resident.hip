@@ -634,6 +634,15 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
       const uint32_t rs8 = (uint32_t)(T * (N + 1) * 8);   // bytes from one slice's words to the next
       const EpiConst kc = epi_const<NS>(a.hc_scale, a.bias);
       const long long t0 = wall_clock64();
+      // From here to the pre poll's end the wave issues at raised priority:
+      // its polls then take the CU's free memory-pipeline slots ahead of the
+      // loads other waves of the CU issue for their next tiles, which
+      // otherwise delay a finaliser's poll by up to several microseconds and
+      // with it every wave waiting for that token's gate (per call after a
+      // cache sweep, n = 4, D = 7168: 50.8 -> 49.5 us at T = 2048 and
+      // 315.6 -> 310.3 us at T = 16384; holding the next loads back instead,
+      // a few in flight per wave at a time, measured 0.3 - 1 us slower).
+      __builtin_amdgcn_s_setprio(3);
       for (; r < 16; r += S) {
         const int64_t tok = (int64_t)tile * kTM + 16 * w + r;
         if (tok >= T) break;
@@ -804,6 +813,7 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
         __builtin_amdgcn_s_sleep(1);
       }
     }
+    if constexpr (STAG) __builtin_amdgcn_s_setprio(0);
     // y column by column, each column's registers refilled with the next
     // tile's residual right after, so those loads overlap the rest of y; the
     // pre step with STAG forms and stores every column of y first, then
