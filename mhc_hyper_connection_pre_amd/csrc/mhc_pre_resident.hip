@@ -108,6 +108,16 @@ __device__ __forceinline__ float tag_val(u64 w) { return __uint_as_float((unsign
 __device__ __forceinline__ u64 count_in(u64* p) {
   return __hip_atomic_fetch_add(p, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
 }
+// Issue priority 3 for waves 0 and 1 of the workgroup, 2 for waves 2 and 3,
+// 1 for 4 and 5, 0 for 6 and 7 (wi: the wave index, uniform).
+__device__ __forceinline__ void set_priority_by_wave(int wi) {
+  switch (__builtin_amdgcn_readfirstlane(wi) >> 1) {
+    case 0: __builtin_amdgcn_s_setprio(3); break;
+    case 1: __builtin_amdgcn_s_setprio(2); break;
+    case 2: __builtin_amdgcn_s_setprio(1); break;
+    default: __builtin_amdgcn_s_setprio(0); break;
+  }
+}
 // Wait until this wave's outstanding vector memory operations (loads and
 // stores) have completed: vmcnt = 0, other counters unconstrained.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0f70); }
@@ -436,7 +446,16 @@ __global__ __launch_bounds__(kThreads, 2) void pre_resident_kernel(ResArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    // The first tile goes out with the lower waves first (issue priority
+    // falling with the wave index): every workgroup then receives the rows of
+    // its first waves early, so the exchanges of those row blocks start while
+    // the later rows still stream in, instead of all of them at the end of
+    // the load phase (per call after a cache sweep at T = 2048, n = 4,
+    // D = 7168: 49.5 -> 48.4 us; the same order for every later tile measured
+    // 48.8 us there).
+    set_priority_by_wave(w);
     load_tile(tile);
+    __builtin_amdgcn_s_setprio(0);
   } else {
     // The first columns of the first generation's residual go out right
     // behind the fn slice (HBM stays busy while B is packed), the rest once B
