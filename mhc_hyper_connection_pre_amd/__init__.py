@@ -2,9 +2,10 @@
 
 A thin Python binding over the C ABI of ``libmhc.so`` (declared in
 ``include/mhc.h``). Every step of the computation runs in the library's HIP
-kernels; this module only checks tensor metadata, allocates outputs and the
-workspace with torch when the caller does not pass them, and marshals
-pointers and the current HIP stream. There is no CPU fallback: if the library
+kernels; this module only checks tensor metadata, allocates outputs with torch
+when the caller does not pass them (and a workspace, kept per device and
+launch stream for later calls), and marshals pointers and the current HIP
+stream. There is no CPU fallback: if the library
 is not built, every call raises.
 
 Functions mirror the C entry points: ``mhc_pre``, ``mhc_post``,
@@ -24,6 +25,7 @@ __all__ = [
     "MhcError", "lib", "library_path", "mhc_pre", "mhc_post", "mhc_post_combine_norm",
     "mhc_pre_workspace_bytes", "mhc_pre_splits", "mhc_pre_sync_timeouts", "mhc_post_pre", "mhc_post_pre_fused",
     "mhc_pre_static", "mhc_pre_plan_info", "MHC_PRE_STATIC_SCRATCH_BYTES", "MHC_BF16", "MHC_F32", "PreparedCall",
+    "release_workspaces",
 ]
 
 MHC_BF16 = 0
@@ -156,6 +158,41 @@ def _stream(device, stream):
     return s.cuda_stream
 
 
+# Workspaces this binding keeps for calls that pass none, one per (device, launch stream). The
+# single-pass kernels carry their state from call to call in the workspace (the last epoch and a
+# shape marker; a call of another shape, or of the two-pass path, re-arms it on the GPU), so the
+# zeroing of its status words at allocation serves every later call and such a call is one
+# launch, not a fill and a launch. Calls on one stream run in order and can share it; calls on
+# another stream get their own. A call made while the current stream is being captured into a
+# graph allocates a fresh workspace, as before (a graph replays with the memory it captured).
+_WORKSPACES: dict = {}
+
+
+def _default_workspace(L, T, n, D, n_splits, dt, dev, stream):
+    torch = _torch()
+    need = max(L.mhc_pre_workspace_bytes(T, n, D, n_splits, dt), 256)
+    if torch.cuda.is_current_stream_capturing():
+        with _on(stream):
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            ws[:256].zero_()
+        return ws
+    key = (dev.index, _stream(dev, stream))
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < need:
+        # allocated and cleared on the launch stream: a smaller one it replaces returns to that
+        # stream's pool, which hands it out again only after the calls queued there
+        with _on(stream):
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            ws[:256].zero_()
+        _WORKSPACES[key] = ws
+    return ws
+
+
+def release_workspaces() -> None:
+    """Drop the workspaces kept for calls that pass none (the memory returns to torch's allocator)."""
+    _WORKSPACES.clear()
+
+
 class PreparedCall:
     """One library call with its tensors checked and its C arguments marshalled once.
 
@@ -242,11 +279,8 @@ def mhc_pre(residual, fn, hc_scale, bias, *, sinkhorn_repeat: int = 20, eps: flo
         post = torch.empty((T, n), dtype=torch.float32, device=dev) if post is None else post
         comb = torch.empty((T, n, n), dtype=torch.float32, device=dev) if comb is None else comb
         y = torch.empty((T, D), dtype=residual.dtype, device=dev) if y is None else y
-        if workspace is None:
-            # a fresh workspace: zeroing the status words makes the kernels clear the rest
-            need = L.mhc_pre_workspace_bytes(T, n, D, n_splits, dt)
-            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-            workspace[:256].zero_()
+    if workspace is None:
+        workspace = _default_workspace(L, T, n, D, n_splits, dt, dev, stream)
     _check(post, (T, n), torch.float32, dev, "post")
     _check(comb, (T, n, n), torch.float32, dev, "comb")
     _check(y, (T, D), residual.dtype, dev, "y")
@@ -363,10 +397,8 @@ def mhc_post_pre(h, residual, post, comb, fn, hc_scale, bias, *, sinkhorn_repeat
         post_next = torch.empty((T, n), dtype=torch.float32, device=dev) if post_next is None else post_next
         comb_next = torch.empty((T, n, n), dtype=torch.float32, device=dev) if comb_next is None else comb_next
         y = torch.empty((T, D), dtype=residual.dtype, device=dev) if y is None else y
-        if workspace is None:
-            need = L.mhc_pre_workspace_bytes(T, n, D, n_splits, dt)
-            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-            workspace[:256].zero_()
+    if workspace is None:
+        workspace = _default_workspace(L, T, n, D, n_splits, dt, dev, stream)
     _check(out, (T, n, D), residual.dtype, dev, "out")
     _check(post_next, (T, n), torch.float32, dev, "post_next")
     _check(comb_next, (T, n, n), torch.float32, dev, "comb_next")

@@ -518,6 +518,59 @@ def test_side_stream_without_workspace():
                      "tensor", f"side stream {k} out")
 
 
+def test_default_workspace_kept_per_stream():
+    """Calls that pass no workspace share one the binding keeps per (device, launch stream): a later call,
+    of the same shape or another, on the same stream reuses it (one launch, no fill) and matches the same
+    call with a fresh workspace of its own bit for bit; another stream gets its own; a call needing more
+    room replaces it; release_workspaces() drops them."""
+    mhc.release_workspaces()
+    xa = W.generate(W.custom(300, 4, 2048, "bf16", seed=51, fn_std=0.02))
+    xb = W.generate(W.custom(64, 4, 5120, "bf16", seed=52, fn_std=0.02))
+    ga, gb = _gpu_inputs(xa), _gpu_inputs(xb)
+
+    def pre(g, **kw):
+        return mhc.mhc_pre(g["residual"], g["fn"], g["hc_scale"], g["bias"], **kw)
+
+    def boundary(g, p, c, **kw):
+        return mhc.mhc_post_pre(g["h"], g["residual"], p, c, g["fn"], g["hc_scale"], g["bias"], **kw)
+
+    def fresh(x):
+        s = x.spec
+        return torch.zeros(max(mhc.mhc_pre_workspace_bytes(s.T, s.n, s.D), 256), dtype=torch.uint8, device="cuda")
+
+    def same(a, b, what):
+        for k, (u, v) in enumerate(zip(a, b)):
+            assert torch.equal(u, v), f"{what}: output {k} differs from the call with its own workspace"
+
+    ref_a = pre(ga, workspace=fresh(xa))
+    ref_b = pre(gb, workspace=fresh(xb))
+    ref_ba = boundary(gb, ref_b[0], ref_b[1], workspace=fresh(xb))
+    cur = torch.cuda.current_stream()
+    for k in range(2):
+        same(pre(ga), ref_a, f"pre A, call {k}")
+    key = (torch.cuda.current_device(), cur.cuda_stream)
+    assert list(mhc._WORKSPACES) == [key]
+    ws0 = mhc._WORKSPACES[key]
+    same(pre(gb), ref_b, "pre B after A")
+    same(boundary(gb, ref_b[0], ref_b[1]), ref_ba, "boundary B")
+    same(pre(ga), ref_a, "pre A after B")
+    need_a = mhc.mhc_pre_workspace_bytes(300, 4, 2048)
+    need_b = mhc.mhc_pre_workspace_bytes(64, 4, 5120)
+    if need_b <= need_a:
+        assert mhc._WORKSPACES[key] is ws0, "a call that fits reuses the stream's workspace"
+    assert mhc._WORKSPACES[key].numel() >= max(need_a, need_b)
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    res = pre(ga, stream=side)
+    side.synchronize()
+    same(res, ref_a, "pre A on a side stream")
+    assert len(mhc._WORKSPACES) == 2
+    mhc.release_workspaces()
+    assert not mhc._WORKSPACES
+    same(pre(ga), ref_a, "pre A after release")
+    mhc.release_workspaces()
+
+
 def test_two_streams_with_their_own_workspaces():
     """Two single-pass calls in flight at once on two streams, each with its own workspace, sized so that
     both grids fit on the chip together (80 + 64 workgroups): neither waits for the other, and each meets
