@@ -49,13 +49,21 @@ hipError_t launch_pack_fn(const PrePlan& p, const float* fn, void* fnp, hipStrea
 // Wave w takes k-steps s_begin + w, + NW, ... (the NW waves read NW adjacent
 // 64-byte segments of every row at a time). Each wave keeps MT x NCB fp32
 // accumulator tiles; the waves are summed in LDS in a fixed order.
-template <int MT, int NW, int NCB, int PF = 3>
-__global__ __launch_bounds__(NW * 64) void pre_gemm_bf16_kernel(const uint16_t* __restrict__ x,
+// PAIR (four waves): waves 0 and 1 store their tiles in LDS, then waves 2
+// and 3 add theirs to the same places, so the sums take half the LDS; with
+// the register budget of two waves per SIMD (and a shorter prefetch ring)
+// two workgroups then share a CU. For n = 8 (eleven column blocks) that
+// doubles the residual loads in flight per CU: T = 2048, D = 7168, each call
+// after a cache sweep, 176 -> 165 us per pre call; T = 16384: 1274 -> 1197 us.
+template <int MT, int NW, int NCB, int PF = 3, bool PAIR = false>
+__global__ __launch_bounds__(NW * 64, PAIR ? 2 : 1) void pre_gemm_bf16_kernel(const uint16_t* __restrict__ x,
                                                                 const u32x4* __restrict__ fnp,
                                                                 float* __restrict__ part, int64_t T, int64_t K,
                                                                 int N, int NP, int ksteps, int steps_per_split) {
   constexpr int CW = NCB * 16 + 1;  // LDS row: padded [hi | lo | lo2] columns, then the sum of squares
-  __shared__ float red[NW * MT * 16 * CW];
+  static_assert(!PAIR || NW == 4, "the paired reduction is written for four waves");
+  constexpr int RW = PAIR ? 2 : NW;   // wave tiles held in LDS at once
+  __shared__ float red[RW * MT * 16 * CW];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int q = lane >> 4;
@@ -148,19 +156,44 @@ __global__ __launch_bounds__(NW * 64) void pre_gemm_bf16_kernel(const uint16_t* 
     ss[mt] += __shfl_xor(ss[mt], 32);
   }
   // C tile layout: lane holds rows 4*q + i (i = 0..3), column r16 of block cb.
-  float* rw = red + w * (MT * 16 * CW);
+  if constexpr (PAIR) {
+    // place (w & 1): wave w & 1 stores, then wave (w & 1) + 2 adds (each lane
+    // to the elements it stored itself), so each place holds w0 + w2 or w1 + w3
+    float* rw = red + (w & 1) * (MT * 16 * CW);
+    for (int ph = 0; ph < 2; ++ph) {
+      if ((w >> 1) == ph) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+        for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
+          for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rw[(mt * 16 + q * 4 + i) * CW + cb * 16 + r16] = acc[mt][cb][i];
-    if (q == 0) rw[(mt * 16 + r16) * CW + NCB * 16] = ss[mt];
+            for (int i = 0; i < 4; ++i) {
+              float& d = rw[(mt * 16 + q * 4 + i) * CW + cb * 16 + r16];
+              d = ph ? d + acc[mt][cb][i] : acc[mt][cb][i];
+            }
+          if (q == 0) {
+            float& d = rw[(mt * 16 + r16) * CW + NCB * 16];
+            d = ph ? d + ss[mt] : ss[mt];
+          }
+        }
+      }
+      __syncthreads();
+    }
+  } else {
+    float* rw = red + w * (MT * 16 * CW);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rw[(mt * 16 + q * 4 + i) * CW + cb * 16 + r16] = acc[mt][cb][i];
+      if (q == 0) rw[(mt * 16 + r16) * CW + NCB * 16] = ss[mt];
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
-  // partial[split][token][c] = sum over waves of (hi + lo (+ lo2 for the
-  // first n columns)) for c < N, squares at c = N.
+  // partial[split][token][c] = sum over the LDS places of (hi + lo (+ lo2
+  // for the first n columns)) for c < N, squares at c = N.
   const int outs = MT * 16 * (N + 1);
   const int npre = n_pre(N);
   for (int idx = threadIdx.x; idx < outs; idx += NW * 64) {
@@ -171,13 +204,13 @@ __global__ __launch_bounds__(NW * 64) void pre_gemm_bf16_kernel(const uint16_t* 
     float v = 0.0f;
     if (c < N) {
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
+      for (int ww = 0; ww < RW; ++ww) {
         const float* r = red + ww * (MT * 16 * CW) + row * CW;
         v += c < npre ? r[c] + r[c + N] + r[c + 2 * N] : r[c] + r[c + N];
       }
     } else {
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) v += red[ww * (MT * 16 * CW) + row * CW + NCB * 16];
+      for (int ww = 0; ww < RW; ++ww) v += red[ww * (MT * 16 * CW) + row * CW + NCB * 16];
     }
     part[((int64_t)split * T + tok) * NP + c] = v;
   }
@@ -224,11 +257,11 @@ __global__ __launch_bounds__(256) void pre_gemm_f32_kernel(const float* __restri
   }
 }
 
-template <int MT, int NW, int NCB>
+template <int MT, int NW, int NCB, int PF = 3, bool PAIR = false>
 static void launch_gemm_bf16(const PrePlan& p, const uint16_t* x, const u32x4* fnp, float* part, hipStream_t s) {
   const dim3 grid((unsigned)((p.T + 16 * MT - 1) / (16 * MT)), (unsigned)p.S);
-  hipLaunchKernelGGL((pre_gemm_bf16_kernel<MT, NW, NCB>), grid, dim3(NW * 64), 0, s, x, fnp, part, p.T, p.K, p.N,
-                     p.NP, p.ksteps, p.steps_per_split);
+  hipLaunchKernelGGL((pre_gemm_bf16_kernel<MT, NW, NCB, PF, PAIR>), grid, dim3(NW * 64), 0, s, x, fnp, part, p.T,
+                     p.K, p.N, p.NP, p.ksteps, p.steps_per_split);
 }
 
 template <int MT, int NW>
@@ -257,11 +290,11 @@ hipError_t launch_pre_gemm(const PrePlan& p, const void* residual, const void* f
   }
   const uint16_t* x = static_cast<const uint16_t*>(residual);
   const u32x4* f = static_cast<const u32x4*>(fnp);
-  if (p.n == 8) {   // 11 column blocks, four waves, MT 16-token tiles per wave
+  if (p.n == 8) {   // 11 column blocks, four waves, MT 16-token tiles per wave, two workgroups per CU
     if (p.MT == 2)
-      launch_gemm_bf16<2, 4, pack_blocks(8)>(p, x, f, part, s);
+      launch_gemm_bf16<2, 4, pack_blocks(8), 2, true>(p, x, f, part, s);
     else
-      launch_gemm_bf16<1, 4, pack_blocks(8)>(p, x, f, part, s);
+      launch_gemm_bf16<1, 4, pack_blocks(8), 2, true>(p, x, f, part, s);
     return hipGetLastError();
   }
   if (p.MT == 1) return launch_gemm_bf16_ncb<1, 16>(p, x, f, part, s);
