@@ -49,14 +49,19 @@ hipError_t launch_pack_fn(const PrePlan& p, const float* fn, void* fnp, hipStrea
 // Wave w takes k-steps s_begin + w, + NW, ... (the NW waves read NW adjacent
 // 64-byte segments of every row at a time). Each wave keeps MT x NCB fp32
 // accumulator tiles; the waves are summed in LDS in a fixed order.
+// Four-wave workgroups get the register budget of two waves per SIMD, so
+// that two of them share a CU: left free, the compiler gave the n = 4 kernel
+// (four 16-token tiles per wave) 160 VGPRs and 128 AGPRs, one wave per SIMD,
+// and a CU then had half the residual loads in flight (per pre call after a
+// cache sweep, T = 16384, n = 4, D = 7168: 462 -> 449 us with 4 splits,
+// 494 -> 459 us with 8; T = 2048 with 4 splits: 88 -> 83.5 us).
 // PAIR (four waves): waves 0 and 1 store their tiles in LDS, then waves 2
-// and 3 add theirs to the same places, so the sums take half the LDS; with
-// the register budget of two waves per SIMD (and a shorter prefetch ring)
-// two workgroups then share a CU. For n = 8 (eleven column blocks) that
-// doubles the residual loads in flight per CU: T = 2048, D = 7168, each call
-// after a cache sweep, 176 -> 165 us per pre call; T = 16384: 1274 -> 1197 us.
+// and 3 add theirs to the same places, so the sums take half the LDS; for
+// n = 8 (eleven column blocks; with a shorter prefetch ring to fit the
+// budget) that is what lets two workgroups share a CU: T = 2048, D = 7168,
+// 176 -> 165 us per pre call; T = 16384: 1274 -> 1197 us.
 template <int MT, int NW, int NCB, int PF = 3, bool PAIR = false>
-__global__ __launch_bounds__(NW * 64, PAIR ? 2 : 1) void pre_gemm_bf16_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void pre_gemm_bf16_kernel(const uint16_t* __restrict__ x,
                                                                 const u32x4* __restrict__ fnp,
                                                                 float* __restrict__ part, int64_t T, int64_t K,
                                                                 int N, int NP, int ksteps, int steps_per_split) {
