@@ -39,7 +39,11 @@
 // its own 16 rows with no workgroup barrier after the prologue: it finalises
 // the tokens of its rows that fall to slice s and polls only for the pre
 // values of its own rows, so waves drift apart and one wave's exchange waits
-// overlap other waves' loads. The tile table picks the instance per shape
+// overlap other waves' loads. Wave priorities order the memory pipeline of
+// a CU there: the first tile is issued lower waves first (each workgroup's
+// first row blocks land early and their exchanges start during the load
+// phase), and a wave polls the exchange at raised priority, ahead of the
+// other waves' next-tile loads. The tile table picks the instance per shape
 // (measured both ways), and a rule on the number of generations covers the
 // rest. The environment variable MHC_STAGGER (0 or 1, read at each launch)
 // forces either instance: a test hook, both give results within the same
